@@ -1,0 +1,109 @@
+/*
+ * libfp8gemm — FP8 (OCP e4m3fn) NT GEMM with fine-grained block scaling and
+ * bf16 output, plus its two MoE grouped layouts, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (DeepGEMM pages: GeekNews summary "Topic Body", which names
+ * DeepSeek-V3 fine-grained scaling and the dense and MoE grouped GEMMs;
+ * flashmla.net "Quick Start Guide", whose operation name reads
+ * fp8 x fp8 -> bf16, "nt"):
+ *
+ *   D[m,n] = bf16( sum_kb  sa[kb][m] * sb[n/128][kb] *
+ *                          sum_{k = 128kb}^{128kb+127}  A[m,k] * B[n,k] )
+ *
+ * "NT": A is [M,K] and B is [N,K], both with K contiguous; D = A * B^T.
+ * The caller supplies FP8 data and any transposition (kakushin.no, "Hvorfor
+ * FP8 og FP4 er interessant").  The 1x128 activation / 128x128 weight scale
+ * granularity is the reading this library implements; the pages say only
+ * "fine-grained".
+ *
+ * Common conventions for every call below
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library keeps no reference after the call returns and allocates nothing.
+ *  - Layouts are row-major with no padding:
+ *      A  : e4m3fn codes, 1 byte each        sa : fp32, [K/128][M] (M contiguous)
+ *      B  : e4m3fn codes, 1 byte each        sb : fp32, [ceil(N/128)][K/128]
+ *      D  : bf16 bit patterns, 2 bytes each
+ *    The last scale block of B covers only the rows that exist when N is not
+ *    a multiple of 128.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are asynchronous on it: a return of FP8GEMM_OK means the work was
+ *    enqueued.  No call synchronises, reads device memory on the host, or
+ *    allocates, so every call may be captured into a HIP graph.
+ *  - Results are rounded once, fp32 -> bf16, to nearest even; NaN inputs give
+ *    NaN outputs.
+ *  - Argument errors are reported synchronously, before anything is launched,
+ *    as a non-zero status; nothing is written then.  No C++ exception crosses
+ *    this interface.  Device-resident index data is never checked on the host
+ *    (that would need a synchronisation): its out-of-range values have the
+ *    defined meanings given per call.
+ *  - Constraints: M, N, K >= 0; K % 128 == 0; A, B and D 16-byte aligned;
+ *    sa and sb 4-byte aligned.  M == 0 or N == 0 returns FP8GEMM_OK without
+ *    launching; K == 0 writes zeros (an empty sum).
+ *  - Calls on different streams may overlap; they share no library state.
+ */
+#ifndef FP8GEMM_H
+#define FP8GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fp8gemm_status {
+  FP8GEMM_OK = 0,
+  FP8GEMM_INVALID_ARG = 1,       /* null pointer for a non-empty problem, negative size, G < 1, expected_m < 0 */
+  FP8GEMM_UNSUPPORTED_SHAPE = 2, /* K % 128 != 0; contiguous layout with M % 128 != 0; sizes past 2^31 elements */
+  FP8GEMM_MISALIGNED = 3,        /* A, B or D not 16-byte aligned, sa or sb not 4-byte aligned */
+  FP8GEMM_LAUNCH_FAILED = 4      /* the HIP runtime refused the launch */
+};
+
+/*
+ * Dense GEMM.  A [M,K], sa [K/128][M], B [N,K], sb [ceil(N/128)][K/128],
+ * D [M,N].  Every element of D is written.
+ */
+int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, const float *sb,
+                                void *D, int M, int N, int K, void *stream);
+
+/*
+ * M-axis contiguous grouped GEMM (GeekNews "성능 평가", contiguous layout:
+ * the experts' rows are stacked along M and share N and K).
+ *   A [M,K] and sa [K/128][M] hold all experts' rows; B [G][N,K] and
+ *   sb [G][ceil(N/128)][K/128] hold one weight matrix per expert; D [M,N].
+ *   m_indices [M] (int32, device) gives each row's expert.  Row m is computed
+ *   with expert m_indices[m]; a row whose index is outside [0,G) (e.g. -1
+ *   for padding) is not written and keeps its previous contents.
+ * Contract: M % 128 == 0, and each aligned 128-row block of A holds rows of
+ * at most one expert (expert segments start at multiples of 128; padding
+ * rows may sit anywhere).  Rows that break it are not written.
+ */
+int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
+                       int M, int N, int K, int G, void *stream, const int32_t *m_indices);
+
+/*
+ * Masked grouped GEMM (GeekNews "성능 평가", masked layout: for graph
+ * replay, where the host cannot know each expert's token count, a device
+ * mask says how many rows of each expert are real and only those are
+ * computed).
+ *   A [G][M,K], sa [G][K/128][M], B [G][N,K], sb [G][ceil(N/128)][K/128],
+ *   D [G][M,N]; M is the per-expert row capacity.
+ *   masked_m [G] (int32, device): expert g's rows m < clamp(masked_m[g], 0, M)
+ *   are computed and written; its other rows keep their previous contents.
+ *   expected_m (host, >= 0) is a hint of the typical masked_m used to choose
+ *   tile shapes; it never changes which elements are written or their values
+ *   beyond the stated tolerance.
+ */
+int grouped_masked(const void *A, const float *sa, const void *B, const float *sb, void *D,
+                   int M, int N, int K, int G, void *stream, const int32_t *masked_m,
+                   int expected_m);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fp8gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H */

@@ -1,0 +1,30 @@
+"""Build libfp8gemm.so in-tree with hipcc for gfx950 (ahead of time; no JIT)."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "fp8gemm.hip")
+LIB = os.path.join(HERE, "libfp8gemm.so")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    # packed fp32 VALU forms are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def command(out=LIB, extra=()):
+    return ["hipcc", *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", out, SRC]
+
+
+def build(out=LIB, extra=()):
+    tmp = out + ".tmp"
+    subprocess.run(command(tmp, extra), check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,327 @@
+// libfp8gemm: FP8 e4m3fn NT GEMM with 1x128 / 128x128 fp32 block scales and
+// bf16 output, dense and MoE grouped (contiguous, masked), for gfx950.
+//
+// Method (DeepGEMM pages, GeekNews summary "Topic Body"): FP8 GEMM with the
+// fine-grained scaling of DeepSeek-V3; the tensor-core partial sum of each
+// scale block is "promoted" into a higher-precision accumulator on the
+// general-purpose cores because FP8 tensor-core accumulation is imprecise.
+// The pages describe that schedule for Hopper (TMA staging, warp
+// specialisation, JIT per shape); none of that is reused.  Here:
+//
+//   * one v_mfma_scale_f32_16x16x128_f8f6f4 (E8M0 scales fixed at 2^0)
+//     covers a whole 128-wide K block of a 16x16 output sub-tile, so its fp32
+//     result IS the block's partial sum: promotion is one VALU FMA per output
+//     element per block, acc += p * (sa * sb), with no extra accumulator tile;
+//   * the MFMA computes the TRANSPOSED sub-tile (weights as the first
+//     operand), so the 4 results a lane holds share one activation row m and
+//     four consecutive weight rows n inside one 128-row scale block: the
+//     combined scale sa[kb][m] * sb[n/128][kb] is one register per lane per
+//     sub-tile column, and the bf16 results of a lane are 8 contiguous bytes
+//     of a row of D;
+//   * A and B tiles are staged global -> registers -> LDS in a two-stage
+//     ring with an XOR swizzle of the 16-byte chunks so that fragment reads
+//     are bank-conflict free;
+//   * the K order inside a block is irrelevant to the sum, so each lane's
+//     32-byte MFMA operand is two 16-byte chunks (c, c+4) of the 128-byte
+//     row and A and B use the same chunk mapping.
+//
+// The grouped layouts reuse the same body (GeekNews "성능 평가"): contiguous
+// tiles look up their expert from m_indices; masked tiles read the expert's
+// device-side row count and tiles past it exit before loading anything.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8gemm.h"
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 128;        // K block = one scale block = one MFMA's K
+constexpr int THREADS = 256;   // 4 waves of 64
+
+enum Layout { DENSE = 0, CONTIG = 1, MASKED = 2 };
+
+struct Args {
+  const uint8_t *A;
+  const float *sa;
+  const uint8_t *B;
+  const float *sb;
+  uint16_t *D;
+  int M, N, K, G;
+  const int32_t *idx;  // m_indices (CONTIG) or masked_m (MASKED)
+  int tiles_m, tiles_n;
+};
+
+// 16-byte chunk position inside a 128-byte LDS row.  Rows r and r+1 share a
+// 256-byte bank window, rows r and r+8 share banks; the XOR key makes any 8
+// consecutive rows, and the 8 even / 8 odd rows of a 16-row fragment, hit
+// distinct chunks.
+__device__ __forceinline__ int chunk_pos(int chunk, int row) {
+  return (chunk ^ ((row ^ (row >> 3)) & 7)) << 4;
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ v8i frag(const uint8_t *row_ptr, int row, int g) {
+  u32x4 lo = *reinterpret_cast<const u32x4 *>(row_ptr + chunk_pos(g, row));
+  u32x4 hi = *reinterpret_cast<const u32x4 *>(row_ptr + chunk_pos(g + 4, row));
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Block tile BM (rows of A / D) x BN (rows of B / columns of D), 4 waves in
+// a 2 x 2 grid, each wave owning (BM/2) x (BN/2).
+template <int BM, int BN, int LAYOUT>
+__global__ __launch_bounds__(THREADS) void gemm_kernel(Args a) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+  constexpr int CA = BM * 8 / THREADS, CB = BN * 8 / THREADS;  // 16-byte chunks per thread
+  static_assert(CA >= 1 && CB >= 1 && WN <= 128 && 128 % WN == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][(BM + BN) * BK];
+  __shared__ int s_group;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int tile = blockIdx.x;
+  const int m0 = (tile % a.tiles_m) * BM, n0 = (tile / a.tiles_m) * BN;
+  const int M = a.M, N = a.N, K = a.K;
+  const int Kb = K / BK, Nb = (N + 127) / 128;
+
+  const uint8_t *A = a.A, *B = a.B;
+  const float *sa = a.sa, *sb = a.sb;
+  uint16_t *D = a.D;
+  int mvalid = M, g = 0;
+  if (LAYOUT == MASKED) {
+    g = blockIdx.y;
+    const int c = a.idx[g];
+    mvalid = c < 0 ? 0 : (c > M ? M : c);
+    if (m0 >= mvalid) return;  // whole tile masked: nothing loaded, nothing written
+    A += (size_t)g * M * K;
+    sa += (size_t)g * Kb * M;
+    D += (size_t)g * M * N;
+  }
+  if (LAYOUT == CONTIG) {
+    if (tid == 0) s_group = -1;
+    __syncthreads();
+    if (tid < BM && m0 + tid < M) {
+      const int v = a.idx[m0 + tid];
+      if (v >= 0 && v < a.G) atomicMax(&s_group, v);
+    }
+    __syncthreads();
+    g = s_group;
+    if (g < 0) return;  // all padding
+  }
+  if (LAYOUT != DENSE) {
+    B += (size_t)g * N * K;
+    sb += (size_t)g * Nb * Kb;
+  }
+
+  // global -> LDS chunk assignment: chunk c = tid + 256 i covers row c/8,
+  // 16-byte column c%8; 8 consecutive threads read one 128-byte line.
+  const uint8_t *gsrc[CA + CB];
+  int ldst[CA + CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + THREADS * i, r = c >> 3, col = c & 7;
+    const int row = min(m0 + r, M - 1);
+    gsrc[i] = A + (size_t)row * K + col * 16;
+    ldst[i] = r * BK + chunk_pos(col, r);
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + THREADS * i, r = c >> 3, col = c & 7;
+    const int row = min(n0 + r, N - 1);
+    gsrc[CA + i] = B + (size_t)row * K + col * 16;
+    ldst[CA + i] = BM * BK + r * BK + chunk_pos(col, r);
+  }
+  u32x4 stage[CA + CB];
+
+  const int fr = lane & 15, fg = lane >> 4;
+  int srow[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) srow[t] = min(m0 + wm * WM + t * 16 + fr, M - 1);
+  const int nb = min((n0 + wn * WN) / 128, Nb - 1);
+  const float *sbp = sb + (size_t)nb * Kb;
+
+  v4f acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (Kb > 0) {
+#pragma unroll
+    for (int i = 0; i < CA + CB; ++i) stage[i] = *reinterpret_cast<const u32x4 *>(gsrc[i]);
+#pragma unroll
+    for (int i = 0; i < CA + CB; ++i) *reinterpret_cast<u32x4 *>(&smem[0][ldst[i]]) = stage[i];
+  }
+  __syncthreads();
+
+  for (int kb = 0; kb < Kb; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < Kb) {
+#pragma unroll
+      for (int i = 0; i < CA + CB; ++i)
+        stage[i] = *reinterpret_cast<const u32x4 *>(gsrc[i] + (size_t)(kb + 1) * BK);
+    }
+    const float sbv = sbp[kb];
+    float s[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) s[t] = sa[(size_t)kb * M + srow[t]] * sbv;
+
+    const uint8_t *As = smem[cur], *Bs = smem[cur] + BM * BK;
+    v8i bfr[TN], afr[TM];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int row = wn * WN + t * 16 + fr;
+      bfr[t] = frag(Bs + row * BK, row, fg);
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int row = wm * WM + t * 16 + fr;
+      afr[t] = frag(As + row * BK, row, fg);
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bfr[i], afr[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], s[j], acc[i][j][r]);
+      }
+
+    if (kb + 1 < Kb) {
+#pragma unroll
+      for (int i = 0; i < CA + CB; ++i)
+        *reinterpret_cast<u32x4 *>(&smem[cur ^ 1][ldst[i]]) = stage[i];
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds D[m][n .. n+3] for each (sub-tile row i, column j)
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + wm * WM + j * 16 + fr;
+    bool ok = m < mvalid;
+    if (LAYOUT == CONTIG) ok = m < M && a.idx[m] == g;
+    if (!ok) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int n = n0 + wn * WN + i * 16 + 4 * fg;
+      uint16_t *dp = D + (size_t)m * N + n;
+      const uint32_t b0 = bf16_bits(acc[i][j][0]), b1 = bf16_bits(acc[i][j][1]);
+      const uint32_t b2 = bf16_bits(acc[i][j][2]), b3 = bf16_bits(acc[i][j][3]);
+      if ((N & 3) == 0 && n + 3 < N) {
+        *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      } else {
+        if (n < N) dp[0] = (uint16_t)b0;
+        if (n + 1 < N) dp[1] = (uint16_t)b1;
+        if (n + 2 < N) dp[2] = (uint16_t)b2;
+        if (n + 3 < N) dp[3] = (uint16_t)b3;
+      }
+    }
+  }
+}
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+template <int BM, int BN, int LAYOUT>
+int launch(Args a, int groups, hipStream_t stream) {
+  a.tiles_m = cdiv(a.M, BM);
+  a.tiles_n = cdiv(a.N, BN);
+  void *kargs[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gemm_kernel<BM, BN, LAYOUT>),
+                                 dim3(a.tiles_m * a.tiles_n, groups), dim3(THREADS), kargs, 0,
+                                 stream);
+  return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Checks shared by the three calls.  Runs before any HIP call.
+int check_common(const void *A, const float *sa, const void *B, const float *sb, const void *D,
+                 int M, int N, int K, long long a_elems, long long b_elems, long long d_elems) {
+  if (M < 0 || N < 0 || K < 0) return FP8GEMM_INVALID_ARG;
+  if (M == 0 || N == 0) return -1;  // empty: nothing to do, success
+  if (!D) return FP8GEMM_INVALID_ARG;
+  if (K > 0 && (!A || !sa || !B || !sb)) return FP8GEMM_INVALID_ARG;  // K == 0 reads nothing
+  if (K % BK != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
+  const long long lim = 1LL << 31;
+  if (a_elems >= lim || b_elems >= lim || d_elems >= lim) return FP8GEMM_UNSUPPORTED_SHAPE;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16) || !aligned(sa, 4) || !aligned(sb, 4))
+    return FP8GEMM_MISALIGNED;
+  return FP8GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, const float *sb,
+                                void *D, int M, int N, int K, void *stream) {
+  const int st = check_common(A, sa, B, sb, D, M, N, K, (long long)M * K, (long long)N * K,
+                              (long long)M * N);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
+         static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= 64) return launch<64, 128, DENSE>(a, 1, s);
+  return launch<128, 128, DENSE>(a, 1, s);
+}
+
+int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
+                       int M, int N, int K, int G, void *stream, const int32_t *m_indices) {
+  if (G < 1) return FP8GEMM_INVALID_ARG;
+  const int st = check_common(A, sa, B, sb, D, M, N, K, (long long)M * K,
+                              (long long)G * N * K, (long long)M * N);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  if (!m_indices) return FP8GEMM_INVALID_ARG;
+  if (!aligned(m_indices, 4)) return FP8GEMM_MISALIGNED;
+  if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
+  Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
+         static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0};
+  return launch<128, 128, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
+}
+
+int grouped_masked(const void *A, const float *sa, const void *B, const float *sb, void *D,
+                   int M, int N, int K, int G, void *stream, const int32_t *masked_m,
+                   int expected_m) {
+  if (G < 1 || expected_m < 0) return FP8GEMM_INVALID_ARG;
+  const int st = check_common(A, sa, B, sb, D, M, N, K, (long long)G * M * K,
+                              (long long)G * N * K, (long long)G * M * N);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  if (!masked_m) return FP8GEMM_INVALID_ARG;
+  if (!aligned(masked_m, 4)) return FP8GEMM_MISALIGNED;
+  if (G > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
+  Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
+         static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (expected_m <= 64) return launch<64, 128, MASKED>(a, G, s);
+  return launch<128, 128, MASKED>(a, G, s);
+}
+
+const char *fp8gemm_status_string(int status) {
+  switch (status) {
+    case FP8GEMM_OK: return "ok";
+    case FP8GEMM_INVALID_ARG: return "invalid argument (null pointer, negative size, G < 1 or expected_m < 0)";
+    case FP8GEMM_UNSUPPORTED_SHAPE: return "unsupported shape (K % 128 != 0, contiguous M % 128 != 0, or too large)";
+    case FP8GEMM_MISALIGNED: return "misaligned pointer (A, B, D need 16 bytes; scales and indices 4)";
+    case FP8GEMM_LAUNCH_FAILED: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

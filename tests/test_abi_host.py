@@ -1,0 +1,87 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments synchronously, before any HIP call
+(every call below fails validation, so nothing is launched)."""
+import ctypes
+
+import pytest
+
+import moe_grouped_gemm_act_amd as fg
+
+OK, INVALID, SHAPE, MISALIGNED = 0, 1, 2, 3
+P = ctypes.c_void_p(0x10000)       # aligned non-null stand-in; never dereferenced
+P_ODD = ctypes.c_void_p(0x10004)   # 4-byte but not 16-byte aligned
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fg.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = fg.declared_functions()
+    assert set(names) == {"gemm_fp8_1x128_128x128_bf16", "grouped_contiguous",
+                          "grouped_masked", "fp8gemm_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert fg.fp8gemm_status_string(s)
+    assert fg.fp8gemm_status_string(99) == "unknown status"
+
+
+def dense(lib, A=P, sa=P, B=P, sb=P, D=P, M=64, N=64, K=128):
+    return lib.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D, M, N, K, NUL)
+
+
+def test_dense_validation(lib):
+    assert dense(lib, M=-1) == INVALID
+    assert dense(lib, N=-5) == INVALID
+    assert dense(lib, K=-128) == INVALID
+    assert dense(lib, A=NUL) == INVALID
+    assert dense(lib, sb=NUL) == INVALID
+    assert dense(lib, D=NUL) == INVALID
+    assert dense(lib, K=100) == SHAPE
+    assert dense(lib, K=129) == SHAPE
+    assert dense(lib, A=P_ODD) == MISALIGNED
+    assert dense(lib, D=P_ODD) == MISALIGNED
+    assert dense(lib, sa=ctypes.c_void_p(0x10002)) == MISALIGNED
+    assert dense(lib, M=1 << 20, K=1 << 12) == SHAPE  # 2^32 elements
+    # empty problems succeed without launching, even with null pointers
+    assert dense(lib, A=NUL, sa=NUL, B=NUL, sb=NUL, D=NUL, M=0) == OK
+    assert dense(lib, A=NUL, sa=NUL, B=NUL, sb=NUL, D=NUL, N=0) == OK
+
+
+def test_contiguous_validation(lib):
+    def call(G=2, M=256, K=128, idx=P, A=P):
+        return lib.grouped_contiguous(A, P, P, P, P, M, 64, K, G, NUL, idx)
+    assert call(G=0) == INVALID
+    assert call(idx=NUL) == INVALID
+    assert call(M=200) == SHAPE
+    assert call(K=64) == SHAPE
+    assert call(idx=ctypes.c_void_p(0x10001)) == MISALIGNED
+    assert call(A=P_ODD) == MISALIGNED
+    assert lib.grouped_contiguous(NUL, NUL, NUL, NUL, NUL, 0, 64, 128, 2, NUL, NUL) == OK
+
+
+def test_masked_validation(lib):
+    def call(G=4, M=256, K=128, mm=P, expected=128):
+        return lib.grouped_masked(P, P, P, P, P, M, 64, K, G, NUL, mm, expected)
+    assert call(G=0) == INVALID
+    assert call(expected=-1) == INVALID
+    assert call(mm=NUL) == INVALID
+    assert call(K=130) == SHAPE
+    assert call(G=1 << 16, M=1, K=128) == SHAPE
+    assert lib.grouped_masked(NUL, NUL, NUL, NUL, NUL, 0, 64, 128, 4, NUL, NUL, 0) == OK
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    A = torch.zeros((4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):  # CPU tensors are refused before the library is called
+        fg.gemm_fp8_1x128_128x128_bf16(A, torch.zeros((1, 4)), torch.zeros((8, 128), dtype=torch.uint8),
+                                       torch.zeros((1, 1)), D=torch.zeros((4, 8), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        fg.gemm_fp8_1x128_128x128_bf16(A.float(), None, None, None)

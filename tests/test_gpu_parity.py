@@ -1,0 +1,315 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+identical seeded inputs.
+
+Small and ragged sizes compare every element; the five workloads at full size
+compare sampled elements the oracle computes one by one, plus whole-tensor
+checks of which elements are written (routing and masking are bit-exact).
+Cases whose fp32 intermediates are exact must match bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_act_amd as fg
+import oracle
+import synth
+from synth import workloads as W
+from parity_util import SENTINEL, assert_close, bits, f32, sentinel_out, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+POOL = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x3C, 0xBC, 0x40, 0xC0], np.uint8)  # 0, +-.5, +-1, +-1.5, +-2
+
+
+def announce(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def gpu_dense(d, D=None):
+    A, sa, B, sb = to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"])
+    if D is None:
+        D = sentinel_out((d["M"], d["N"]))
+    fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
+    torch.cuda.synchronize()
+    return bits(D)
+
+
+def gpu_contig(d):
+    D = sentinel_out((d["M"], d["N"]))
+    fg.grouped_contiguous(to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"]),
+                          to_gpu(d["m_indices"]), D)
+    torch.cuda.synchronize()
+    return bits(D)
+
+
+def gpu_masked(d, expected_m=None):
+    D = sentinel_out((d["G"], d["M"], d["N"]))
+    fg.grouped_masked(to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"]),
+                      to_gpu(d["masked_m"]), d.get("expected_m", 128) if expected_m is None else expected_m, D)
+    torch.cuda.synchronize()
+    return bits(D)
+
+
+def same_values(a, b):
+    """bitwise equal up to the sign of zero"""
+    fa, fb = f32(a), f32(b)
+    return bool(((fa == fb) | (np.isnan(fa) & np.isnan(fb))).all())
+
+
+def sample_points(rng, M, N, count, tile=128):
+    """random (m, n) plus tile and scale-block boundary rows/columns"""
+    ms = [0, 1, M - 1] + [x for t in range(tile, M, tile) for x in (t - 1, t)][:16]
+    ns = [0, 1, N - 1] + [x for t in range(128, N, 128) for x in (t - 1, t)][:16]
+    bm = np.array([m for m in ms if 0 <= m < M] * len(ns))
+    bn = np.repeat([n for n in ns if 0 <= n < N], len([m for m in ms if 0 <= m < M]))
+    pm = np.concatenate([rng.integers(0, M, count), bm])
+    pn = np.concatenate([rng.integers(0, N, count), bn])
+    return pm, pn
+
+
+# ------------------------------------------------------------------ dense ----
+
+
+def test_small_workload_full():
+    M, N, K = W.SMALL
+    announce(f"dense small {M}x{N}x{K} seed 1000")
+    d = W.dense(1000, M, N, K)
+    assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), "small")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 100, 256), (64, 2112, 384), (65, 130, 128),
+                                   (129, 257, 512), (300, 520, 640), (128, 2112, 1024),
+                                   (200, 96, 128), (256, 2048, 256)])
+def test_dense_ragged_full(M, N, K):
+    seed = 1100 + M + N + K
+    announce(f"dense ragged {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K)
+    assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), f"{M}x{N}x{K}")
+
+
+def test_dense_exact_power_of_two():
+    rng = np.random.default_rng(21)
+    M, N, K = 160, 2112, 512
+    A = rng.choice(POOL, (M, K))
+    B = rng.choice(POOL, (N, K))
+    sa = (2.0 ** rng.integers(-2, 3, (K // 128, M))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-2, 3, (17, K // 128))).astype(np.float32)
+    sb[16] *= 8  # the partial last block (columns 2048..2111)
+    announce("dense exact power-of-two 160x2112x512")
+    d = {"A": A, "sa": sa, "B": B, "sb": sb, "M": M, "N": N, "K": K}
+    assert same_values(gpu_dense(d), oracle.gemm(A, sa, B, sb))
+
+
+def test_dense_identity_and_permutation_exact():
+    rng = np.random.default_rng(22)
+    M, N, K = 192, 300, 256
+    perm = rng.permutation(K)[:M]
+    A = np.zeros((M, K), np.uint8)
+    A[np.arange(M), perm] = 0x38
+    B = rng.choice(np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8), (N, K))
+    sa = np.ones((K // 128, M), np.float32)
+    sb = (2.0 ** rng.integers(-4, 5, (3, K // 128))).astype(np.float32)
+    announce("dense permutation 192x300x256")
+    d = {"A": A, "sa": sa, "B": B, "sb": sb, "M": M, "N": N, "K": K}
+    assert same_values(gpu_dense(d), oracle.gemm(A, sa, B, sb))
+
+
+def test_dense_zero_k_writes_zeros():
+    announce("dense K=0")
+    d = {"A": np.zeros((70, 0), np.uint8), "sa": np.zeros((0, 70), np.float32),
+         "B": np.zeros((40, 0), np.uint8), "sb": np.zeros((1, 0), np.float32), "M": 70, "N": 40, "K": 0}
+    assert (f32(gpu_dense(d)) == 0).all()
+
+
+def test_dense_nan_propagates():
+    rng = np.random.default_rng(23)
+    d = W.dense(1201, 96, 160, 256)
+    d["A"][5, 17] = 0x7F
+    d["B"][150, 200] = 0xFF
+    announce("dense NaN 96x160x256")
+    out = gpu_dense(d)
+    ref = oracle.gemm(d["A"], d["sa"], d["B"], d["sb"])
+    assert (np.isnan(f32(out)) == np.isnan(f32(ref))).all()
+    assert_close(out, ref, "nan case")
+    del rng
+
+
+def test_dense_deterministic_and_stream():
+    d = W.dense(1300, 128, 2112, 1024)
+    announce("dense determinism 128x2112x1024")
+    a = gpu_dense(d)
+    b = gpu_dense(d)
+    s = torch.cuda.Stream()
+    A, sa, B, sb = to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"])
+    D = sentinel_out((128, 2112))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
+    s.synchronize()
+    assert (a == b).all() and (bits(D) == a).all()
+
+
+@pytest.mark.parametrize("M,N,K", W.DECODE_SHAPES)
+def test_decode_workload_sampled(M, N, K):
+    seed = 2000 + W.DECODE_SHAPES.index((M, N, K))
+    announce(f"decode {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K)
+    out = gpu_dense(d)
+    assert (out != SENTINEL).all()
+    rng = np.random.default_rng(seed)
+    pm, pn = sample_points(rng, M, N, 4000)
+    # plus two whole rows
+    pm = np.concatenate([pm, np.zeros(N, int), np.full(N, M - 1)])
+    pn = np.concatenate([pn, np.arange(N), np.arange(N)])
+    ref = oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn)
+    assert_close(out[pm, pn], ref, f"decode {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", W.PREFILL_SHAPES)
+def test_prefill_workload_sampled(M, N, K):
+    seed = 3000 + W.PREFILL_SHAPES.index((M, N, K))
+    announce(f"prefill {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K, heavy=True)
+    out = gpu_dense(d)
+    assert (out != SENTINEL).all()
+    rng = np.random.default_rng(seed)
+    pm, pn = sample_points(rng, M, N, 6000)
+    heavy = np.flatnonzero(synth.heavy_rows(seed + 7, M) != 1)
+    pm = np.concatenate([pm, np.repeat(heavy, 20)])
+    pn = np.concatenate([pn, rng.integers(0, N, 20 * len(heavy))])
+    ref = oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn)
+    assert_close(out[pm, pn], ref, f"prefill {M}x{N}x{K}")
+
+
+# ------------------------------------------------------------- contiguous ---
+
+
+def test_contiguous_small_full():
+    d = W.contiguous(4100, 3, 128 * 5, 160, 256, uniform=False)
+    announce("contiguous G=3 640x160x256")
+    out = gpu_contig(d)
+    ref = oracle.grouped_contiguous(d["A"], d["sa"], d["B"], d["sb"], d["m_indices"],
+                                    np.full((d["M"], d["N"]), SENTINEL, np.uint16))
+    pad = d["m_indices"] < 0
+    assert (out[pad] == SENTINEL).all() and (out[~pad] != SENTINEL).all()
+    assert_close(out[~pad], ref[~pad], "contiguous small")
+
+
+def test_contiguous_edge_cases():
+    G, N, K, M = 4, 200, 256, 128 * 6
+    idx = np.full(M, -1, np.int32)
+    idx[0:100] = 2          # expert 2, padded tail
+    idx[128:256] = 0        # full tile of expert 0
+    # rows 256..383: a whole tile of padding; expert 1 has no rows
+    idx[384:500] = 3
+    idx[512:640] = 0        # expert 0 again, second segment
+    idx[640:700] = 3
+    idx[650] = 99           # out of range: treated as padding
+    idx[651] = -5
+    d = W.dense(4200, M, N, K)
+    B, sb = synth.grouped_weight(4201, G, N, K)
+    d.update(B=B, sb=sb, m_indices=idx, G=G)
+    announce("contiguous edge cases")
+    out = gpu_contig(d)
+    ref = oracle.grouped_contiguous(d["A"], d["sa"], B, sb, idx, np.full((M, N), SENTINEL, np.uint16))
+    valid = (idx >= 0) & (idx < G)
+    assert (out[~valid] == SENTINEL).all() and (out[valid] != SENTINEL).all()
+    assert_close(out[valid], ref[valid], "contiguous edges")
+
+
+def test_contiguous_routing_probe_exact():
+    G, N, K, M = 8, 128, 128, 128 * 8
+    B = np.zeros((G, N, K), np.uint8)
+    B[:, np.arange(N), np.arange(K)] = 0x38
+    sb = np.stack([np.full((1, 1), 2.0 ** g, np.float32) for g in range(G)])
+    A = np.zeros((M, K), np.uint8)
+    A[np.arange(M), np.arange(M) % K] = 0x38
+    sa = np.ones((1, M), np.float32)
+    idx = np.repeat(np.array([5, 2, 7, 0, 1, 6, 3, 4], np.int32), 128)
+    idx[np.arange(M) % 128 >= 120] = -1
+    d = {"A": A, "sa": sa, "B": B, "sb": sb, "m_indices": idx, "M": M, "N": N, "K": K, "G": G}
+    announce("contiguous routing probe")
+    out = gpu_contig(d)
+    ref = oracle.grouped_contiguous(A, sa, B, sb, idx, np.full((M, N), SENTINEL, np.uint16))
+    assert (out == ref).all()
+
+
+@pytest.mark.parametrize("case", range(len(W.CONTIG_CASES)))
+def test_contiguous_workload_sampled(case):
+    G, rows, N, K, uniform = W.CONTIG_CASES[case]
+    seed = 4000 + case
+    announce(f"contiguous G={G} {rows}x{N}x{K} uniform={uniform} seed {seed}")
+    d = W.contiguous(seed, G, rows, N, K, uniform)
+    out = gpu_contig(d)
+    idx = d["m_indices"]
+    pad = idx < 0
+    assert (out[pad] == SENTINEL).all(), "padding row written"
+    assert (out[~pad] != SENTINEL).all(), "valid row not written"
+    rng = np.random.default_rng(seed)
+    pm, pn = sample_points(rng, rows, N, 6000)
+    for start, plen, valid in d["segments"]:  # first and last valid row of every expert
+        pm = np.concatenate([pm, [start, start + valid - 1] * 8])
+        pn = np.concatenate([pn, rng.integers(0, N, 16)])
+    keep = idx[pm] >= 0
+    pm, pn = pm[keep], pn[keep]
+    ref = oracle.points("contiguous", d["A"], d["sa"], d["B"], d["sb"], pm, pn, m_indices=idx)
+    assert_close(out[pm, pn], ref, f"contiguous G={G}")
+
+
+# ----------------------------------------------------------------- masked ---
+
+
+def test_masked_small_full():
+    G, M, N, K = 6, 200, 130, 256
+    d = W.masked(5100, G, M, N, K)
+    d["masked_m"] = np.array([0, 1, 63, 200, 250, -3], np.int32)
+    announce("masked small G=6 200x130x256")
+    out = gpu_masked(d, expected_m=64)
+    ref = oracle.grouped_masked(d["A"], d["sa"], d["B"], d["sb"], d["masked_m"],
+                                np.full((G, M, N), SENTINEL, np.uint16))
+    written = np.arange(M)[None, :] < np.clip(d["masked_m"], 0, M)[:, None]
+    assert (out[~written] == SENTINEL).all() and (out[written] != SENTINEL).all()
+    assert_close(out[written], ref[written], "masked small")
+
+
+def test_masked_count_sweep_and_hint():
+    counts = np.array([0, 1, 63, 64, 127, 128, 129, 255, 256], np.int32)
+    G, M, N, K = len(counts), 256, 256, 384
+    d = W.masked(5200, G, M, N, K)
+    d["masked_m"] = counts
+    ref = oracle.grouped_masked(d["A"], d["sa"], d["B"], d["sb"], counts,
+                                np.full((G, M, N), SENTINEL, np.uint16))
+    written = np.arange(M)[None, :] < counts[:, None]
+    outs = []
+    for em in (0, 32, 128, 256):
+        announce(f"masked sweep expected_m={em}")
+        out = gpu_masked(d, expected_m=em)
+        assert (out[~written] == SENTINEL).all() and (out[written] != SENTINEL).all()
+        assert_close(out[written], ref[written], f"masked sweep em={em}")
+        outs.append(out)
+
+
+@pytest.mark.parametrize("case", range(len(W.MASKED_CASES)))
+def test_masked_workload_sampled(case):
+    G, M, N, K = W.MASKED_CASES[case]
+    seed = 5000 + case
+    announce(f"masked G={G} {M}x{N}x{K} seed {seed}")
+    d = W.masked(seed, G, M, N, K)
+    out = gpu_masked(d)
+    mm = d["masked_m"]
+    written = np.arange(M)[None, :] < mm[:, None]
+    assert (out[~written] == SENTINEL).all(), "masked row written"
+    assert (out[written] != SENTINEL).all(), "unmasked row not written"
+    rng = np.random.default_rng(seed)
+    gs = np.flatnonzero(mm > 0)
+    cnt = 8000
+    pg = rng.choice(gs, cnt)
+    pm = (rng.random(cnt) * mm[pg]).astype(np.int64)
+    pn = rng.integers(0, N, cnt)
+    pg = np.concatenate([pg, gs, gs])
+    pm = np.concatenate([pm, np.zeros(len(gs), int), mm[gs] - 1])
+    pn = np.concatenate([pn, rng.integers(0, N, 2 * len(gs))])
+    ref = oracle.points("masked", d["A"], d["sa"], d["B"], d["sb"], pm, pn, pg=pg)
+    assert_close(out[pg, pm, pn], ref, f"masked G={G} N={N} K={K}")
