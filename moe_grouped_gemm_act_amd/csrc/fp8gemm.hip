@@ -32,6 +32,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+
 #include "fp8gemm.h"
 
 namespace {
@@ -236,7 +242,306 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M kernel (decode shapes, M <= 128): the weights are the HBM stream.
+//
+// A workgroup owns MROWS = 16 * MG activation rows, BN = 64 * NBW weight
+// rows and a range of K blocks; wave w owns weight rows [w BN/4, (w+1) BN/4)
+// and all activation rows.  Each K block's activation and weight tiles are
+// read with whole 128-byte rows per 8 lanes (a wave instruction covers 8
+// full lines: the L1 path sustains about 3.5x the bandwidth it gives to
+// MFMA-fragment-shaped requests, which touch 16 half lines each) into a
+// two-slot swizzled LDS ring, staged through registers two blocks ahead;
+// the MFMA fragments are then read from LDS.  Loads past the end of the K
+// range use buffer offsets beyond the resource, which return zeros without
+// touching memory.
+//
+// When the output alone gives too few workgroups to cover the chip, K is
+// also split over `splits` workgroups per output tile: each writes its fp32
+// partial tile to a workspace with coherent (sc1) stores, waits for them to
+// land, and counts in on a per-tile counter; the last to arrive reads the
+// other partials with coherent loads, adds all of them in split order,
+// rounds to bf16, stores, and re-arms the counter.  The result is
+// deterministic, and no agent-wide cache writeback or invalidate is issued
+// (those flush the whole L2 of an XCD).
+struct SkArgs {
+  const uint8_t *A;
+  const float *sa;
+  const uint8_t *B;
+  const float *sb;
+  uint16_t *D;
+  int M, N, K;
+  int splits, kb_per_split;
+  float *ws;
+  unsigned *counters;
+};
+
+constexpr uint32_t OOB = 0x80000000u;  // buffer offset past any resource: reads zeros
+#ifndef SK_RS
+#define SK_RS 2  // register sets: K blocks staged ahead (deeper measured slower on MI355X)
+#endif
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+template <int MG, int NBW, int RS>
+__global__ __launch_bounds__(THREADS) void skinny_kernel(SkArgs a) {
+  constexpr int MROWS = 16 * MG, BN = 64 * NBW;
+  constexpr int U = RS % 2 == 0 ? RS : 2 * RS;  // loop unroll: register set and LDS slot indices static
+  constexpr int CH = (MROWS + BN) * 8 / THREADS;  // 16-byte chunks per thread per K block
+  constexpr int CHA = MROWS * 8 / THREADS;         // of which activation chunks (the first ones)
+  constexpr int SLOT = (MROWS + BN) * BK;
+  static_assert(MROWS * 8 % THREADS == 0 && BN * 8 % THREADS == 0 && 128 % BN == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][SLOT];
+  __shared__ float ssa[2][THREADS];  // sa of the slot's K block; entries >= MROWS unused
+  __shared__ float ssb[2][THREADS];  // sb of the slot's K block, replicated (no ALU on loads
+                                     // before they reach LDS: the compiler would hoist it)
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, fg = lane >> 4;
+  const int ntile = blockIdx.x, split = blockIdx.y, mtile = blockIdx.z;
+  const int n0 = ntile * BN, m0 = mtile * MROWS;
+  const int M = a.M, N = a.N, K = a.K, Kb = K / BK;
+  const int kb0 = split * a.kb_per_split;
+  const int kb1 = min(Kb, kb0 + a.kb_per_split);
+  const int nk = max(kb1 - kb0, 0);
+
+  const __amdgpu_buffer_rsrc_t ra = rsrc(a.A, (uint32_t)M * K);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, (uint32_t)N * K);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(a.sa, (uint32_t)M * Kb * 4);
+  // chunk i of this thread: row r = c / 8 of the slot (activation rows first), 16-byte column c % 8
+  uint32_t goff[CH];
+  int loff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = tid + THREADS * i, r = c >> 3, col = c & 7;
+    const int grow = r < MROWS ? min(m0 + r, M - 1) : min(n0 + r - MROWS, N - 1);
+    goff[i] = (uint32_t)grow * K + col * 16;
+    loff[i] = r * BK + chunk_pos(col, r);
+  }
+  const uint32_t soff = (uint32_t)min(m0 + tid, M - 1) * 4;
+  const __amdgpu_buffer_rsrc_t rsb = rsrc(a.sb + (size_t)(n0 / 128) * Kb, (uint32_t)Kb * 4);
+
+  u32x4 st[RS][CH];
+  float sst[RS], sbt[RS];
+  // G(t): global -> registers, K block kb0 + t, register set t % RS (zeros past the range)
+#define SK_G(t)                                                                               \
+  do {                                                                                        \
+    const bool ok_ = (t) < nk;                                                                \
+    const uint32_t ko_ = ok_ ? (uint32_t)(kb0 + (t)) * BK : OOB;                              \
+    sst[(t) % RS] = __builtin_bit_cast(                                                       \
+        float, __builtin_amdgcn_raw_buffer_load_b32(                                          \
+                   rs, ok_ ? soff + (uint32_t)(kb0 + (t)) * M * 4 : OOB, 0, 0));              \
+    sbt[(t) % RS] = __builtin_bit_cast(                                                       \
+        float, __builtin_amdgcn_raw_buffer_load_b32(                                          \
+                   rsb, ok_ ? (uint32_t)(kb0 + (t)) * 4 : OOB, 0, 0));                        \
+    _Pragma("unroll") for (int i = 0; i < CH; ++i) st[(t) % RS][i] = __builtin_bit_cast(     \
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < CHA ? ra : rb, goff[i] + ko_, 0, 0)); \
+  } while (0)
+  // W(t): register set t % RS -> LDS slot t & 1
+#define SK_W(t)                                                                               \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < CH; ++i)                                            \
+        *reinterpret_cast<u32x4 *>(&lds[(t) & 1][loff[i]]) = st[(t) % RS][i];                 \
+    ssa[(t) & 1][tid] = sst[(t) % RS];                                                        \
+    ssb[(t) & 1][tid] = sbt[(t) % RS]; /* the same value in every entry */                    \
+  } while (0)
+
+  v4f acc[NBW][MG];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+#pragma unroll
+    for (int i = 0; i < MG; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Block t: loaded G(t) RS - 1 iterations before it is written to LDS,
+  // W(t) one iteration before it is used.
+#pragma unroll
+  for (int t = 0; t < RS; ++t) SK_G(t);
+  SK_W(0);
+  SK_G(RS);
+  for (int t = 0; t < nk; t += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // t % U == 0, so every set / slot index below is static
+      const int tt = t + u;
+      __syncthreads();      // slot tt&1 written; nobody still reads slot (tt+1)&1
+      SK_W(tt + 1);
+      SK_G(tt + 1 + RS);
+      const uint8_t *sl = lds[u & 1];
+      v8i bfr[NBW];
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int row = MROWS + (wave * NBW + j) * 16 + fr;
+        bfr[j] = frag(sl + row * BK, row, fg);
+      }
+#pragma unroll
+      for (int i = 0; i < MG; ++i) {
+        const int row = i * 16 + fr;
+        const v8i afr = frag(sl + row * BK, row, fg);
+        const float s = ssa[u & 1][row] * ssb[u & 1][row];
+        v4f pr[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+          pr[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bfr[j], afr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(pr[j][r], s, acc[j][i][r]);
+      }
+    }
+  }
+#undef SK_G
+#undef SK_W
+
+  if (a.splits > 1) {
+    const int tile = mtile * gridDim.x + ntile;
+    constexpr int PER = THREADS * NBW * MG * 4;  // floats per partial tile
+    float *part = a.ws + (size_t)tile * a.splits * PER;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int i = 0; i < MG; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(part + (size_t)split * PER + (((j * MG + i) * 4 + r) * THREADS + tid),
+                             acc[j][i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before this workgroup counts in
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.splits - 1);
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int i = 0; i < MG; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float t = 0.f;
+          for (int s = 0; s < a.splits; ++s)
+            t += s == split ? acc[j][i][r]
+                            : __hip_atomic_load(
+                                  part + (size_t)s * PER + (((j * MG + i) * 4 + r) * THREADS + tid),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          acc[j][i][r] = t;
+        }
+    if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+#pragma unroll
+  for (int i = 0; i < MG; ++i) {
+    const int m = m0 + i * 16 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int n = n0 + (wave * NBW + j) * 16 + 4 * fg;
+      uint16_t *dp = a.D + (size_t)m * N + n;
+      const uint32_t b0 = bf16_bits(acc[j][i][0]), b1 = bf16_bits(acc[j][i][1]);
+      const uint32_t b2 = bf16_bits(acc[j][i][2]), b3 = bf16_bits(acc[j][i][3]);
+      if ((N & 3) == 0 && n + 3 < N) {
+        *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      } else {
+        if (n < N) dp[0] = (uint16_t)b0;
+        if (n + 1 < N) dp[1] = (uint16_t)b1;
+        if (n + 2 < N) dp[2] = (uint16_t)b2;
+        if (n + 3 < N) dp[3] = (uint16_t)b3;
+      }
+    }
+  }
+}
+
 int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---- split-K workspace: one per (device, stream), made on first need ------
+// Holds fp32 partial tiles and per-tile arrival counters (zeroed once here,
+// re-armed by the kernels).  Never allocated while the stream is capturing:
+// such calls run without a K split instead.
+constexpr size_t WS_FLOATS = size_t(16) << 20;  // 64 MB of partials
+constexpr int WS_COUNTERS = 1 << 16;
+
+struct Workspace {
+  float *part = nullptr;
+  unsigned *counters = nullptr;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+const Workspace *workspace(hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws.find({dev, s});
+  if (it != g_ws.end()) return &it->second;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  Workspace w;
+  if (hipMalloc(reinterpret_cast<void **>(&w.part), WS_FLOATS * sizeof(float)) != hipSuccess)
+    return nullptr;
+  if (hipMalloc(reinterpret_cast<void **>(&w.counters), WS_COUNTERS * sizeof(unsigned)) != hipSuccess ||
+      hipMemsetAsync(w.counters, 0, WS_COUNTERS * sizeof(unsigned), s) != hipSuccess) {
+    (void)hipFree(w.part);
+    return nullptr;
+  }
+  return &(g_ws[{dev, s}] = w);
+}
+
+// Optional override for tuning sweeps: FP8GEMM_SKINNY="nbw,splits" (nbw: 16-row
+// weight groups per wave, 1 or 2).
+bool skinny_override(int *nbw, int *splits) {
+  const char *e = getenv("FP8GEMM_SKINNY");
+  return e && sscanf(e, "%d,%d", nbw, splits) == 2 && (*nbw == 1 || *nbw == 2) && *splits >= 1;
+}
+
+template <int MG, int NBW>
+int launch_skinny(SkArgs a, int m_tiles, int n_tiles, hipStream_t stream) {
+  void *kargs[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&skinny_kernel<MG, NBW, SK_RS>),
+                                 dim3(n_tiles, a.splits, m_tiles), dim3(THREADS), kargs, 0, stream);
+  return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+}
+
+// Dense GEMM with at most 128 activation rows per m-tile.
+int run_skinny(const uint8_t *A, const float *sa, const uint8_t *B, const float *sb, uint16_t *D,
+               int M, int N, int K, hipStream_t stream) {
+  const int MG = M <= 64 ? 4 : 8;
+  const int m_tiles = cdiv(M, 16 * MG);
+  const int Kb = K / BK;
+  int nbw = 1, splits = 1;
+  if (!skinny_override(&nbw, &splits)) {
+    // measured on MI355X (decode shapes, weights streamed from HBM): one
+    // 16-row weight group per wave; a two-way K split pays for its partial
+    // exchange only when there are few output tiles
+    nbw = 1;
+    const int tiles = cdiv(N, 64) * m_tiles;
+    splits = tiles < 100 ? 2 : 1;
+  }
+  const int n_tiles = cdiv(N, 64 * nbw);
+  splits = std::max(1, std::min(splits, std::max(Kb, 1)));
+  const int kps = Kb > 0 ? cdiv(Kb, splits) : 0;
+  splits = Kb > 0 ? cdiv(Kb, kps) : 1;
+  SkArgs a{A, sa, B, sb, D, M, N, K, splits, kps, nullptr, nullptr};
+  if (splits > 1) {
+    const Workspace *w = workspace(stream);
+    const size_t need = (size_t)n_tiles * m_tiles * splits * 16 * MG * 64 * nbw;
+    if (!w || need > WS_FLOATS || n_tiles * m_tiles > WS_COUNTERS) {
+      a.splits = 1;
+      a.kb_per_split = Kb;
+    } else {
+      a.ws = w->part;
+      a.counters = w->counters;
+    }
+  }
+  if (MG == 4)
+    return nbw == 2 ? launch_skinny<4, 2>(a, m_tiles, n_tiles, stream)
+                    : launch_skinny<4, 1>(a, m_tiles, n_tiles, stream);
+  return nbw == 2 ? launch_skinny<8, 2>(a, m_tiles, n_tiles, stream)
+                  : launch_skinny<8, 1>(a, m_tiles, n_tiles, stream);
+}
 
 template <int BM, int BN, int LAYOUT>
 int launch(Args a, int groups, hipStream_t stream) {
@@ -278,7 +583,8 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= 64) return launch<64, 128, DENSE>(a, 1, s);
+  if (M <= 128)
+    return run_skinny(a.A, sa, a.B, sb, a.D, M, N, K, s);
   return launch<128, 128, DENSE>(a, 1, s);
 }
 
