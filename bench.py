@@ -3,7 +3,8 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one pass of the hot path over one batch of the workload: one GEMM
-call per shape of the workload, inputs already resident in HBM.  The default
+call per shape of the workload, inputs already resident in HBM, launched as a
+HIP graph replay (the decode regime's launch mode).  The default
 workload is the decode-shaped dense set (M in {64, 128} x (N, K) in
 {(2112,7168), (24576,1536), (7168,2048), (4096,7168)}), which is memory-bound:
 `value` is algorithmic bytes moved per second (GB/s) over the timed steps,
@@ -11,10 +12,10 @@ counting A, B, the scales and D once per call.  Every step uses a different
 copy of the inputs (rotating sets totalling > 1 GB) so weights come from HBM,
 not from the 256 MB last-level cache.
 
-Rank 0 prints one JSON line.  Extra fields: per-shape kernel times from HIP
-events recorded around every launch in the timed region on the launch
-stream, the roofline of the dominant shape's kernel, and the CPU oracle timed
-on a bounded sample of the same workload.
+Rank 0 prints one JSON line.  Extra fields: per-shape kernel times (HIP
+events on the launch stream around back-to-back graph replays of that
+shape's kernel), the roofline of the dominant shape's kernel, and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -62,14 +63,26 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM: copy a MIB-sized buffer 5 times (a plain copy "
+                         "kernel of known size, used to calibrate rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU form "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return
 
     import moe_grouped_gemm_act_amd as fg
     from synth import workloads as W
@@ -77,11 +90,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shapes = workload_shapes(args.workload)
+    stream = torch.cuda.Stream(dev)
 
     # inputs: one seeded set per shape, cloned on the GPU into rotating copies
-    sets = []
-    total = 0
-    host = []
+    sets, host, total = [], [], 0
     for i, (_, M, N, K, heavy) in enumerate(shapes):
         d = W.dense(2000 + i if args.workload == "decode" else 3000 + i, M, N, K, heavy=heavy)
         host.append(d)
@@ -90,44 +102,65 @@ def main():
         sets.append([t])
         total += dense_bytes(M, N, K)
     copies = max(1, min(64, -(-ROTATE_BYTES // total)))
-    for s in sets:
+    for s_ in sets:
         for _ in range(copies - 1):
-            s.append({k: v.clone() for k, v in s[0].items()})
+            s_.append({k: v.clone() for k, v in s_[0].items()})
     torch.cuda.synchronize()
 
-    def step(j, events=None):
-        for i, s in enumerate(sets):
-            t = s[j % copies]
-            if events is not None:
-                events[i][0].record()
-            fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
-            if events is not None:
-                events[i][1].record()
+    def launch(i, j):
+        t = sets[i][j % copies]
+        fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
 
-    for j in range(args.warmup):
-        step(j)
-    torch.cuda.synchronize()
-
-    # timed region: wall clock around exactly K steps; events on the launch
-    # stream (torch's current stream, which the binding launches on)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)] for _ in shapes]
+    # Steps run as HIP graph replays (one graph per rotation set, all shapes in
+    # order), so the timed region measures the GPU, not Python launch cost.
+    with torch.cuda.stream(stream):
+        for j in range(copies):  # eager first: any per-stream workspace is made outside capture
+            for i in range(len(shapes)):
+                launch(i, j)
+    stream.synchronize()
+    step_graphs = []
+    for j in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(len(shapes)):
+                launch(i, j)
+        step_graphs.append(g)
+    with torch.cuda.stream(stream):
+        for j in range(args.warmup):
+            step_graphs[j % copies].replay()
+    stream.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j in range(args.steps):
-        step(j, [ev[i][j] for i in range(len(shapes))])
+    with torch.cuda.stream(stream):
+        for j in range(args.steps):
+            step_graphs[j % copies].replay()
+    stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # per-shape kernel duration: HIP events on the launch stream around
+    # back-to-back replays of a graph holding `copies` launches of that shape
     per_shape = []
+    reps = max(3, min(50, args.steps // 4))
     for i, (_, M, N, K, _) in enumerate(shapes):
-        ms = np.array([a.elapsed_time(b) for a, b in ev[i]])
-        avg_s = float(ms.mean()) * 1e-3
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for j in range(copies):
+                launch(i, j)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+        stream.synchronize()
+        avg_s = a.elapsed_time(b) * 1e-3 / (reps * copies)
         by, fl = dense_bytes(M, N, K), 2.0 * M * N * K
         per_shape.append({"M": M, "N": N, "K": K, "avg_us": avg_s * 1e6,
-                          "median_us": float(np.median(ms)) * 1e3,
                           "GBps": by / avg_s / 1e9, "TFLOPS": fl / avg_s / 1e12,
                           "bytes": by, "flop": fl})
+        del g
     dom = max(per_shape, key=lambda r: r["avg_us"])
     step_bytes = sum(r["bytes"] for r in per_shape)
     step_flop = sum(r["flop"] for r in per_shape)
@@ -142,6 +175,7 @@ def main():
                 "unit": "TFLOP/s", "frac": dom["TFLOPS"] / PEAK_FP8_TFLOPS, "traffic": None}
     roof["kernel"] = f"dense {dom['M']}x{dom['N']}x{dom['K']}"
     roof["avg_us"] = dom["avg_us"]
+    roof["traffic"] = measured_traffic(roof["kernel"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -168,6 +202,23 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch (calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE) for
+    `kernel`, from the committed profile summaries -- only when they were taken
+    on the kernel source as it is now; otherwise None."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc", "fp8gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.json"))):
+        d = json.load(open(f))
+        k = d.get("kernels", {}).get(kernel)
+        if d.get("source_sha256") == sha and k:
+            return {"bytes": k["fetch_bytes"] + k["write_bytes"], "fetch_bytes": k["fetch_bytes"],
+                    "write_bytes": k["write_bytes"], "source": os.path.basename(f)}
+    return None
+
+
 def cpu_baseline(host, shapes, budget_s, memory_bound):
     """The oracle, as it stands, on whole outputs of the workload's shapes
     (in order) until about budget_s seconds of wall time have been spent."""
@@ -176,24 +227,30 @@ def cpu_baseline(host, shapes, budget_s, memory_bound):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    done, by, fl = [], 0, 0.0
-    for d, (_, M, N, K, _) in zip(host, shapes):
-        if done and time.perf_counter() - t0 > budget_s:
+    done, by, fl, passes = [], 0, 0.0, 0
+    while True:
+        for d, (_, M, N, K, _) in zip(host, shapes):
+            # whole output rows, as many as the remaining budget allows at an
+            # assumed 1e9 multiply-adds per second per thread
+            left = max(0.2, budget_s - (time.perf_counter() - t0))
+            rows = max(1, min(M, int(left * 1e9 * threads / (N * K))))
+            A, sa = d["A"][:rows], np.ascontiguousarray(d["sa"][:, :rows])
+            oracle.gemm(A, sa, d["B"], d["sb"], threads=threads)
+            if passes == 0:
+                done.append(f"{rows}x{N}x{K}")
+            by += dense_bytes(rows, N, K)  # algorithmic bytes of the computed slice
+            fl += 2.0 * rows * N * K
+            if time.perf_counter() - t0 > budget_s:
+                break
+        passes += 1
+        if time.perf_counter() - t0 > budget_s:
             break
-        # whole output rows, as many as the remaining budget allows at an
-        # assumed 2e8 multiply-adds per second per thread
-        left = max(0.5, budget_s - (time.perf_counter() - t0))
-        rows = max(1, min(M, int(left * 2e8 * threads / (N * K))))
-        A, sa = d["A"][:rows], np.ascontiguousarray(d["sa"][:, :rows])
-        oracle.gemm(A, sa, d["B"], d["sb"], threads=threads)
-        done.append(f"{rows}x{N}x{K}")
-        by += dense_bytes(rows, N, K)  # algorithmic bytes of the computed slice
-        fl += 2.0 * rows * N * K
     dt = time.perf_counter() - t0
     val = by / dt / 1e9 if memory_bound else fl / dt / 1e12
     return {"value": val, "unit": "GB/s" if memory_bound else "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": dt, "gflops": fl / dt / 1e9,
-            "sample": "full outputs (all columns) of the first rows of each shape: " + ", ".join(done)}
+            "sample": f"{passes} pass(es) over whole output rows of each shape (first pass: "
+                      + ", ".join(done) + f"), stopped after about {budget_s:.0f} s"}
 
 
 if __name__ == "__main__":
