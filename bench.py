@@ -37,22 +37,74 @@ def dense_bytes(M, N, K):
     return M * K + N * K + 4 * M * Kb + 4 * Nb * Kb + 2 * M * N
 
 
-def workload_shapes(name):
+def grouped_cost(rows_per_group, N, K):
+    """Algorithmic FLOP and bytes of a grouped call: only valid rows, and the
+    weights of experts that have at least one row."""
+    Kb, Nb = K // 128, (N + 127) // 128
+    rows = sum(rows_per_group)
+    live = sum(1 for r in rows_per_group if r > 0)
+    flop = 2.0 * rows * N * K
+    by = rows * K + 4 * rows * Kb + live * (N * K + 4 * Nb * Kb) + 2 * rows * N
+    return flop, by
+
+
+class Call:
+    """One GEMM call of a workload: seeded host inputs, device copies, cost."""
+
+    def __init__(self, kind, d, label, flop, by):
+        self.kind, self.d, self.label, self.flop, self.bytes = kind, d, label, flop, by
+
+    def to_device(self, torch, dev):
+        keys = ["A", "sa", "B", "sb"] + (["m_indices"] if self.kind == "contiguous" else []) \
+            + (["masked_m"] if self.kind == "masked" else [])
+        t = {k: torch.from_numpy(self.d[k]).to(dev) for k in keys}
+        shape = (self.d["G"], self.d["M"], self.d["N"]) if self.kind == "masked" else (self.d["M"], self.d["N"])
+        t["D"] = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        return t
+
+    def launch(self, fg, t):
+        if self.kind == "dense":
+            fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
+        elif self.kind == "contiguous":
+            fg.grouped_contiguous(t["A"], t["sa"], t["B"], t["sb"], t["m_indices"], t["D"])
+        else:
+            fg.grouped_masked(t["A"], t["sa"], t["B"], t["sb"], t["masked_m"], self.d["expected_m"], t["D"])
+
+
+def workload_calls(name):
+    import numpy as np
     from synth import workloads as W
-    if name == "decode":
-        return [("dense", M, N, K, False) for (M, N, K) in W.DECODE_SHAPES]
-    if name == "prefill":
-        return [("dense", M, N, K, True) for (M, N, K) in W.PREFILL_SHAPES]
-    if name == "small":
-        return [("dense",) + W.SMALL + (False,)]
-    raise SystemExit(f"unknown workload {name}")
+    calls = []
+    if name in ("decode", "prefill", "small"):
+        shapes = {"decode": W.DECODE_SHAPES, "prefill": W.PREFILL_SHAPES, "small": (W.SMALL,)}[name]
+        for i, (M, N, K) in enumerate(shapes):
+            seed = {"decode": 2000, "prefill": 3000, "small": 1000}[name] + i
+            d = W.dense(seed, M, N, K, heavy=name == "prefill")
+            calls.append(Call("dense", d, f"dense {M}x{N}x{K}", 2.0 * M * N * K, dense_bytes(M, N, K)))
+    elif name == "contiguous":
+        for i, (G, rows, N, K, uniform) in enumerate(W.CONTIG_CASES):
+            d = W.contiguous(4000 + i, G, rows, N, K, uniform)
+            counts = np.bincount(d["m_indices"][d["m_indices"] >= 0], minlength=G)
+            flop, by = grouped_cost(counts.tolist(), N, K)
+            calls.append(Call("contiguous", d, f"contiguous G={G} {rows}x{N}x{K}", flop, by + 4 * rows))
+    elif name == "masked":
+        for i, (G, M, N, K) in enumerate(W.MASKED_CASES):
+            d = W.masked(5000 + i, G, M, N, K)
+            flop, by = grouped_cost(np.clip(d["masked_m"], 0, M).tolist(), N, K)
+            calls.append(Call("masked", d, f"masked G={G} {M}x{N}x{K}", flop, by + 4 * G))
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return calls
 
 
 WORKLOAD_TEXT = {
     "decode": "dense decode-shaped FP8 GEMM, M in {64,128} x (N,K) in {(2112,7168),(24576,1536),(7168,2048),(4096,7168)}",
     "prefill": "dense prefill-shaped FP8 GEMM, M=4096 x (N,K) in {(7168,16384),(2112,7168),(24576,1536),(7168,18432)}, 1% rows x50",
     "small": "dense FP8 GEMM 128x256x512",
+    "contiguous": "MoE grouped FP8 GEMM, M-axis contiguous: G=4 x 8192 rows and G=8 uneven (32768 padded rows), N=4096, K=7168",
+    "masked": "MoE grouped FP8 GEMM, masked: G=16, 256 rows/expert, masked_m ~ U[0,256], (N,K) in {(4096,7168),(7168,2048)}",
 }
+MEMORY_BOUND = {"decode", "small", "masked"}
 
 
 def main():
@@ -89,18 +141,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    shapes = workload_shapes(args.workload)
+    calls = workload_calls(args.workload)
     stream = torch.cuda.Stream(dev)
 
-    # inputs: one seeded set per shape, cloned on the GPU into rotating copies
-    sets, host, total = [], [], 0
-    for i, (_, M, N, K, heavy) in enumerate(shapes):
-        d = W.dense(2000 + i if args.workload == "decode" else 3000 + i, M, N, K, heavy=heavy)
-        host.append(d)
-        t = {k: torch.from_numpy(d[k]).to(dev) for k in ("A", "sa", "B", "sb")}
-        t["D"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        sets.append([t])
-        total += dense_bytes(M, N, K)
+    # inputs: one seeded set per call, cloned on the GPU into rotating copies
+    sets, total = [], 0
+    for c in calls:
+        sets.append([c.to_device(torch, dev)])
+        total += c.bytes
     copies = max(1, min(64, -(-ROTATE_BYTES // total)))
     for s_ in sets:
         for _ in range(copies - 1):
@@ -108,21 +156,20 @@ def main():
     torch.cuda.synchronize()
 
     def launch(i, j):
-        t = sets[i][j % copies]
-        fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
+        calls[i].launch(fg, sets[i][j % copies])
 
-    # Steps run as HIP graph replays (one graph per rotation set, all shapes in
+    # Steps run as HIP graph replays (one graph per rotation set, all calls in
     # order), so the timed region measures the GPU, not Python launch cost.
     with torch.cuda.stream(stream):
         for j in range(copies):  # eager first: any per-stream workspace is made outside capture
-            for i in range(len(shapes)):
+            for i in range(len(calls)):
                 launch(i, j)
     stream.synchronize()
     step_graphs = []
     for j in range(copies):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for i in range(len(shapes)):
+            for i in range(len(calls)):
                 launch(i, j)
         step_graphs.append(g)
     with torch.cuda.stream(stream):
@@ -138,11 +185,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per-shape kernel duration: HIP events on the launch stream around
-    # back-to-back replays of a graph holding `copies` launches of that shape
-    per_shape = []
+    # per-call kernel duration: HIP events on the launch stream around
+    # back-to-back replays of a graph holding `copies` launches of that call
+    per_call = []
     reps = max(3, min(50, args.steps // 4))
-    for i, (_, M, N, K, _) in enumerate(shapes):
+    for i, c in enumerate(calls):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for j in range(copies):
@@ -156,15 +203,13 @@ def main():
             b.record(stream)
         stream.synchronize()
         avg_s = a.elapsed_time(b) * 1e-3 / (reps * copies)
-        by, fl = dense_bytes(M, N, K), 2.0 * M * N * K
-        per_shape.append({"M": M, "N": N, "K": K, "avg_us": avg_s * 1e6,
-                          "GBps": by / avg_s / 1e9, "TFLOPS": fl / avg_s / 1e12,
-                          "bytes": by, "flop": fl})
+        per_call.append({"call": c.label, "avg_us": avg_s * 1e6, "GBps": c.bytes / avg_s / 1e9,
+                         "TFLOPS": c.flop / avg_s / 1e12, "bytes": c.bytes, "flop": c.flop})
         del g
-    dom = max(per_shape, key=lambda r: r["avg_us"])
-    step_bytes = sum(r["bytes"] for r in per_shape)
-    step_flop = sum(r["flop"] for r in per_shape)
-    memory_bound = args.workload in ("decode", "small")
+    dom = max(per_call, key=lambda r: r["avg_us"])
+    step_bytes = sum(c.bytes for c in calls)
+    step_flop = sum(c.flop for c in calls)
+    memory_bound = args.workload in MEMORY_BOUND
     gbps = step_bytes * args.steps / wall / 1e9
     tflops = step_flop * args.steps / wall / 1e12
     if memory_bound:
@@ -173,13 +218,13 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": dom["TFLOPS"], "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": dom["TFLOPS"] / PEAK_FP8_TFLOPS, "traffic": None}
-    roof["kernel"] = f"dense {dom['M']}x{dom['N']}x{dom['K']}"
+    roof["kernel"] = dom["call"]
     roof["avg_us"] = dom["avg_us"]
     roof["traffic"] = measured_traffic(roof["kernel"])
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host, shapes, args.cpu_seconds, memory_bound)
+        cpu = cpu_baseline(calls, args.cpu_seconds, memory_bound)
 
     line = {
         "metric": METRIC,
@@ -189,13 +234,13 @@ def main():
         "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "shapes": len(shapes),
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "calls": len(calls),
                    "rotating_copies": copies, "parallelism": "none (1 GPU)"},
         "tflops": tflops,
         "frac_fp8_peak": tflops / PEAK_FP8_TFLOPS,
         "gbps": gbps,
         "frac_hbm_peak": gbps / PEAK_HBM_GBS,
-        "per_shape": per_shape,
+        "per_call": per_call,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -219,9 +264,10 @@ def measured_traffic(kernel):
     return None
 
 
-def cpu_baseline(host, shapes, budget_s, memory_bound):
-    """The oracle, as it stands, on whole outputs of the workload's shapes
-    (in order) until about budget_s seconds of wall time have been spent."""
+def cpu_baseline(calls, budget_s, memory_bound):
+    """The oracle, as it stands, on whole output rows of the workload's dense
+    calls (in order, repeated) until about budget_s seconds of wall time have
+    been spent; grouped calls are sampled as dense GEMMs of one expert."""
     import numpy as np
 
     import oracle
@@ -229,13 +275,20 @@ def cpu_baseline(host, shapes, budget_s, memory_bound):
     t0 = time.perf_counter()
     done, by, fl, passes = [], 0, 0.0, 0
     while True:
-        for d, (_, M, N, K, _) in zip(host, shapes):
+        for c in calls:
+            d = c.d
+            A, sa, B, sb = d["A"], d["sa"], d["B"], d["sb"]
+            if c.kind == "masked":
+                A, sa, B, sb = A[0], sa[0], B[0], sb[0]
+            elif c.kind == "contiguous":
+                B, sb = B[0], sb[0]
+            M, K = A.shape
+            N = B.shape[0]
             # whole output rows, as many as the remaining budget allows at an
             # assumed 1e9 multiply-adds per second per thread
             left = max(0.2, budget_s - (time.perf_counter() - t0))
             rows = max(1, min(M, int(left * 1e9 * threads / (N * K))))
-            A, sa = d["A"][:rows], np.ascontiguousarray(d["sa"][:, :rows])
-            oracle.gemm(A, sa, d["B"], d["sb"], threads=threads)
+            oracle.gemm(A[:rows], np.ascontiguousarray(sa[:, :rows]), B, sb, threads=threads)
             if passes == 0:
                 done.append(f"{rows}x{N}x{K}")
             by += dense_bytes(rows, N, K)  # algorithmic bytes of the computed slice
@@ -249,7 +302,7 @@ def cpu_baseline(host, shapes, budget_s, memory_bound):
     val = by / dt / 1e9 if memory_bound else fl / dt / 1e12
     return {"value": val, "unit": "GB/s" if memory_bound else "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": dt, "gflops": fl / dt / 1e9,
-            "sample": f"{passes} pass(es) over whole output rows of each shape (first pass: "
+            "sample": f"{passes} pass(es) over whole output rows of each call (first pass: "
                       + ", ".join(done) + f"), stopped after about {budget_s:.0f} s"}
 
 

@@ -63,13 +63,14 @@ struct Args {
   int tiles_m, tiles_n;
 };
 
-// 16-byte chunk position inside a 128-byte LDS row.  Rows r and r+1 share a
-// 256-byte bank window, rows r and r+8 share banks; the XOR key makes any 8
-// consecutive rows, and the 8 even / 8 odd rows of a 16-row fragment, hit
-// distinct chunks.
-__device__ __forceinline__ int chunk_pos(int chunk, int row) {
-  return (chunk ^ ((row ^ (row >> 3)) & 7)) << 4;
-}
+// XOR key of an LDS row: 16-byte chunk c of row r sits at position
+// c ^ key(r).  Rows r and r+1 share a 256-byte bank window and rows r, r+8
+// share banks; this key makes any 8 consecutive rows, and the 8 even / 8 odd
+// rows of a 16-row fragment, hit distinct chunks.  It depends on r mod 16
+// only, so every 16-row fragment of a tile has the same per-lane pattern and
+// the compiler can address all of them from one base with immediate offsets.
+__device__ __forceinline__ int row_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int chunk_pos(int chunk, int row) { return (chunk ^ row_key(row)) << 4; }
 
 // fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
@@ -227,6 +228,231 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Args a) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int n = n0 + wn * WN + i * 16 + 4 * fg;
+      uint16_t *dp = D + (size_t)m * N + n;
+      const uint32_t b0 = bf16_bits(acc[i][j][0]), b1 = bf16_bits(acc[i][j][1]);
+      const uint32_t b2 = bf16_bits(acc[i][j][2]), b3 = bf16_bits(acc[i][j][3]);
+      if ((N & 3) == 0 && n + 3 < N) {
+        *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      } else {
+        if (n < N) dp[0] = (uint16_t)b0;
+        if (n + 1 < N) dp[1] = (uint16_t)b1;
+        if (n + 2 < N) dp[2] = (uint16_t)b2;
+        if (n + 3 < N) dp[3] = (uint16_t)b3;
+      }
+    }
+  }
+}
+
+// Direct-to-LDS loads (global_load_lds): each lane's `bytes` from global
+// memory land at lds + lane * bytes.  Kept in a device function: written in a
+// kernel template, the builtin makes the host pass drop the kernel's stub.
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt: bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their no-wait maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
+
+// ---------------------------------------------------------------------------
+// Large-M kernel (prefill and MoE grouped shapes): compute bound.
+//
+// Block tile BN = WGN * TN * 16 weight rows by BM = WGM * TM * 16 activation
+// rows.  Six waves: four compute waves in a WGN x WGM grid, each owning a
+// (TN * 16) x (TM * 16) tile (per K block it reads TN + TM operand fragments
+// from LDS for TN * TM MFMAs), and two loader waves.  The loaders move each
+// K block's activation rows, weight rows and activation scales with
+// direct-to-LDS loads (global_load_lds: 16 bytes per lane, one 128-byte row
+// per 8 lanes, the lane -> source mapping applying the XOR swizzle) into a
+// ring of STAGES slots, STAGES - 1 blocks ahead, and wait for them with an
+// explicit vmcnt; one bare barrier per K block hands a slot over.  Because
+// vector-memory counters are per wave, the compute waves never wait on the
+// loads in flight (they issue none), and the loaders never stall on LDS
+// reads.  The weight scales of the tile's K range sit in LDS, loaded once.
+constexpr int TK_THREADS = 384;
+
+template <int WGN, int WGM, int TN, int TM, int STAGES, int LAYOUT>
+__global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
+  constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int SLOT = ROWS * BK + BM * 4;  // operand rows, then the BM activation scales
+  constexpr int OCT = ROWS / 8;             // 1 KB row groups per slot
+  constexpr int DMA = OCT / 2;              // row-group loads per loader wave per slot
+  constexpr int SDMA = BM / 128;            // 64-float scale loads per loader wave per slot
+  constexpr int PER_G = DMA + SDMA;         // vector memory instructions per loader per slot
+  constexpr int MAXKB = 160;                // K <= 20480 for the weight-scale preload
+  static_assert(WGN * WGM == 4 && OCT % 2 == 0 && BM % 128 == 0 && 128 % (TN * 16) == 0,
+                "tile shape");
+  static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
+  __shared__ float s_sb[BN > 128 ? 2 : 1][MAXKB];
+  __shared__ int s_group;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, fg = lane >> 4;
+  const int M = a.M, N = a.N, K = a.K, Kb = K / BK, Nb = (N + 127) / 128;
+
+  // tile order: workgroup ids are dealt to the 8 XCDs round robin; give each
+  // XCD a contiguous run of tiles, walked GROUPN weight tiles at a time with
+  // the activation tiles inside, so concurrent tiles on one XCD share panels
+  constexpr int GROUPN = 4;
+  const int T = a.tiles_m * a.tiles_n;
+  int tile = blockIdx.x;
+  {
+    const int x = tile % 8, l = tile / 8, per = T / 8, rem = T % 8;
+    tile = x * per + min(x, rem) + l;
+  }
+  int tn, tm;
+  {
+    const int gsz = GROUPN * a.tiles_m, grp = tile / gsz, in = tile % gsz;
+    const int gw = min(GROUPN, a.tiles_n - grp * GROUPN);
+    tn = grp * GROUPN + in % gw;
+    tm = in / gw;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint8_t *A = a.A, *B = a.B;
+  const float *sa = a.sa, *sb = a.sb;
+  uint16_t *D = a.D;
+  int mvalid = M, g = 0;
+  if (LAYOUT == MASKED) {
+    g = blockIdx.y;
+    const int c = a.idx[g];
+    mvalid = c < 0 ? 0 : (c > M ? M : c);
+    if (m0 >= mvalid) return;  // whole tile masked: nothing loaded, nothing written
+    A += (size_t)g * M * K;
+    sa += (size_t)g * Kb * M;
+    D += (size_t)g * M * N;
+  }
+  if (LAYOUT == CONTIG) {
+    if (tid == 0) s_group = -1;
+    __syncthreads();
+    if (tid < BM && m0 + tid < M) {
+      const int v = a.idx[m0 + tid];
+      if (v >= 0 && v < a.G) atomicMax(&s_group, v);
+    }
+    __syncthreads();
+    g = s_group;
+    if (g < 0) return;  // all padding
+  }
+  if (LAYOUT != DENSE) {
+    B += (size_t)g * N * K;
+    sb += (size_t)g * Nb * Kb;
+  }
+  for (int i = tid; i < (BN > 128 ? 2 : 1) * Kb; i += TK_THREADS) {
+    const int h = i / Kb, kb = i % Kb;
+    s_sb[h][kb] = sb[(size_t)min(n0 / 128 + h, Nb - 1) * Kb + kb];
+  }
+
+  if (wave >= 4) {
+    // ---------------- loader waves ----------------
+    const int L = wave - 4;
+    // q-th row-group load: rows (L + 2q) * 8 .. + 7 of the slot; lane l ->
+    // row + l / 8, physical chunk l % 8 holding logical chunk (l % 8) ^ key(row)
+    uint32_t off[DMA];  // byte offsets from A (rows < BM) or B (the rest); < 2^31
+#pragma unroll
+    for (int q = 0; q < DMA; ++q) {
+      const int r = (L + 2 * q) * 8 + (lane >> 3);
+      const int col = (lane & 7) ^ row_key(r);
+      off[q] = (uint32_t)(r < BM ? min(m0 + r, M - 1) : min(n0 + r - BM, N - 1)) * K + col * 16;
+    }
+    uint32_t soff[SDMA];  // scale floats (L + 2j) * 64 + lane of the tile's rows
+#pragma unroll
+    for (int j = 0; j < SDMA; ++j) soff[j] = (uint32_t)min(m0 + (L + 2 * j) * 64 + lane, M - 1);
+    // G(t): K block t (clamped: blocks past the end re-read the last one and
+    // are never consumed) -> slot t % STAGES
+#define TK_G(t)                                                                               \
+  do {                                                                                        \
+    const int kb_ = min((t), Kb - 1);                                                         \
+    uint8_t *sl_ = lds[(t) % STAGES];                                                         \
+    _Pragma("unroll") for (int q = 0; q < DMA; ++q)                                          \
+        dma16(((L + 2 * q) * 8 < BM ? A : B) + off[q] + (uint32_t)kb_ * BK,                   \
+              sl_ + (L + 2 * q) * 1024);                                                      \
+    _Pragma("unroll") for (int j = 0; j < SDMA; ++j)                                          \
+        dma4(sa + soff[j] + (uint32_t)kb_ * M, sl_ + ROWS * BK + (L + 2 * j) * 256);          \
+  } while (0)
+    __syncthreads();  // weight scales visible (before any load is in flight: this
+                      // barrier drains the vector-memory queue)
+    if (Kb > 0) {
+#pragma unroll
+      for (int t = 0; t < STAGES - 1; ++t) TK_G(t);
+    }
+    for (int t0 = 0; t0 < Kb; t0 += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) {
+        const int t = t0 + u;
+        if (t >= Kb) break;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_G * (STAGES - 2)));  // my loads of block t landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and everyone's; all compute waves are past block t - 1
+        asm volatile("" ::: "memory");
+        TK_G(t + STAGES - 1);
+      }
+    }
+#undef TK_G
+    __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int wn = wave % WGN, wm = wave / WGN;
+  const int hsb = (wn * TN * 16) / 128;  // which weight-scale block this wave's rows use
+  v4f acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // weight scales visible
+
+  for (int t0 = 0; t0 < Kb; t0 += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) {
+      const int t = t0 + u;
+      if (t >= Kb) break;
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // block t is in slot u
+      asm volatile("" ::: "memory");
+      const uint8_t *sl = lds[u];
+      const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
+      const float sbv = s_sb[hsb][t];
+      v8i bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int row = BM + (wn * TN + i) * 16 + fr;
+        bfr[i] = frag(sl + row * BK, row, fg);
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int row = (wm * TM + j) * 16 + fr;
+        const v8i afr = frag(sl + row * BK, row, fg);
+        const float sc = ssl[row] * sbv;
+        v4f pr[TN];
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          pr[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bfr[i], afr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[i][r], sc, acc[i][j][r]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + (wm * TM + j) * 16 + fr;
+    bool ok = m < mvalid;
+    if (LAYOUT == CONTIG) ok = m < M && a.idx[m] == g;
+    if (!ok) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int n = n0 + (wn * TN + i) * 16 + 4 * fg;
       uint16_t *dp = D + (size_t)m * N + n;
       const uint32_t b0 = bf16_bits(acc[i][j][0]), b1 = bf16_bits(acc[i][j][1]);
       const uint32_t b2 = bf16_bits(acc[i][j][2]), b3 = bf16_bits(acc[i][j][3]);
@@ -543,6 +769,17 @@ int run_skinny(const uint8_t *A, const float *sa, const uint8_t *B, const float 
                   : launch_skinny<8, 1>(a, m_tiles, n_tiles, stream);
 }
 
+template <int WGN, int WGM, int TN, int TM, int STAGES, int LAYOUT>
+int launch_tile(Args a, int groups, hipStream_t stream) {
+  a.tiles_m = cdiv(a.M, WGM * TM * 16);
+  a.tiles_n = cdiv(a.N, WGN * TN * 16);
+  void *kargs[] = {&a};
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, LAYOUT>),
+      dim3(a.tiles_m * a.tiles_n, groups), dim3(TK_THREADS), kargs, 0, stream);
+  return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+}
+
 template <int BM, int BN, int LAYOUT>
 int launch(Args a, int groups, hipStream_t stream) {
   a.tiles_m = cdiv(a.M, BM);
@@ -585,7 +822,8 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= 128)
     return run_skinny(a.A, sa, a.B, sb, a.D, M, N, K, s);
-  return launch<128, 128, DENSE>(a, 1, s);
+  if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
+  return launch_tile<2, 2, 4, 8, 3, DENSE>(a, 1, s);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -599,7 +837,8 @@ int grouped_contiguous(const void *A, const float *sa, const void *B, const floa
   if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0};
-  return launch<128, 128, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
+  if (K > 20480) return launch<128, 128, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
+  return launch_tile<4, 1, 4, 8, 3, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
 }
 
 int grouped_masked(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -615,8 +854,8 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (expected_m <= 64) return launch<64, 128, MASKED>(a, G, s);
-  return launch<128, 128, MASKED>(a, G, s);
+  if (expected_m <= 64 || K > 20480) return launch<64, 128, MASKED>(a, G, s);
+  return launch_tile<2, 2, 4, 8, 3, MASKED>(a, G, s);
 }
 
 const char *fp8gemm_status_string(int status) {
