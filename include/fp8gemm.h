@@ -20,7 +20,7 @@
  * Common conventions for every call below
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers owned by the caller; the
- *    library keeps no reference after the call returns and allocates nothing.
+ *    library keeps no reference after the call returns.
  *  - Layouts are row-major with no padding:
  *      A  : e4m3fn codes, 1 byte each        sa : fp32, [K/128][M] (M contiguous)
  *      B  : e4m3fn codes, 1 byte each        sb : fp32, [ceil(N/128)][K/128]
@@ -29,8 +29,16 @@
  *    a multiple of 128.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls are asynchronous on it: a return of FP8GEMM_OK means the work was
- *    enqueued.  No call synchronises, reads device memory on the host, or
- *    allocates, so every call may be captured into a HIP graph.
+ *    enqueued.  No call synchronises or reads device memory on the host, so
+ *    every call may be captured into a HIP graph.
+ *  - Library-owned memory: the dense call with M <= 128 may split K over
+ *    several workgroups and then needs a workspace (64 MB of fp32 partial
+ *    tiles and 256 KB of arrival counters).  It is allocated with hipMalloc
+ *    the first time a call on a given (device, stream) needs it, kept until
+ *    the process ends, and never allocated while the stream is capturing: a
+ *    call made during capture before the stream has a workspace runs
+ *    without a K split (same results within the tolerance, slower).  If the
+ *    allocation fails the call also runs without a K split.
  *  - Results are rounded once, fp32 -> bf16, to nearest even; NaN inputs give
  *    NaN outputs.
  *  - Argument errors are reported synchronously, before anything is launched,
@@ -41,7 +49,8 @@
  *  - Constraints: M, N, K >= 0; K % 128 == 0; A, B and D 16-byte aligned;
  *    sa and sb 4-byte aligned.  M == 0 or N == 0 returns FP8GEMM_OK without
  *    launching; K == 0 writes zeros (an empty sum).
- *  - Calls on different streams may overlap; they share no library state.
+ *  - Calls on different streams may overlap: each (device, stream) has its
+ *    own workspace.  Calls on one stream are ordered by the stream.
  */
 #ifndef FP8GEMM_H
 #define FP8GEMM_H
