@@ -18,9 +18,14 @@
 //     combined scale sa[kb][m] * sb[n/128][kb] is one register per lane per
 //     sub-tile column, and the bf16 results of a lane are 8 contiguous bytes
 //     of a row of D;
-//   * A and B tiles are staged global -> registers -> LDS in a two-stage
-//     ring with an XOR swizzle of the 16-byte chunks so that fragment reads
-//     are bank-conflict free;
+//   * A and B tiles are staged into an LDS ring by dedicated loader waves
+//     with direct-to-LDS loads (the Hopper design's asynchronous copies and
+//     warp specialisation become wave roles on one workgroup barrier), with
+//     an XOR swizzle of the 16-byte chunks so that fragment reads are
+//     bank-conflict free;
+//   * decode shapes (M <= 128) stream the weights from HBM: the same kernel
+//     with 64-row tiles and, where the output gives too few tiles to keep
+//     every CU streaming, a deterministic split of K;
 //   * the K order inside a block is irrelevant to the sum, so each lane's
 //     32-byte MFMA operand is two 16-byte chunks (c, c+4) of the 128-byte
 //     row and A and B use the same chunk mapping.
@@ -61,6 +66,9 @@ struct Args {
   int M, N, K, G;
   const int32_t *idx;  // m_indices (CONTIG) or masked_m (MASKED)
   int tiles_m, tiles_n;
+  int splits, kb_per_split;  // K split over workgroups (tile kernel, dense only); 1 and K/128 otherwise
+  float *ws;                 // split-K partial tiles and arrival counters (splits > 1)
+  unsigned *counters;
 };
 
 // XOR key of an LDS row: 16-byte chunk c of row r sits at position
@@ -89,6 +97,10 @@ __device__ __forceinline__ v8i frag(const uint8_t *row_ptr, int row, int g) {
   return r;
 }
 
+// Fallback kernel for shapes the tile kernel does not take (K > 20480, past
+// its weight-scale preload; masked calls with small expected counts, where
+// 64-row tiles waste less): A and B staged global -> registers -> LDS in a
+// two-slot ring.
 // Block tile BM (rows of A / D) x BN (rows of B / columns of D), 4 waves in
 // a 2 x 2 grid, each wave owning (BM/2) x (BN/2).
 template <int BM, int BN, int LAYOUT>
@@ -253,60 +265,81 @@ __device__ __forceinline__ void dma4(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
 }
 
+// Buffer resource over [p, p + bytes): raw buffer loads past the end return
+// zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;  // buffer cache-policy bit: device-coherent access (sc1)
+constexpr uint32_t OOB = 0x80000000u;  // buffer offset past any resource: reads zeros
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (vmcnt: bits 3:0 and 15:14; expcnt and lgkmcnt
 // left at their no-wait maxima)
 constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
 
 // ---------------------------------------------------------------------------
-// Large-M kernel (prefill and MoE grouped shapes): compute bound.
+// Tile kernel: every shape except the fallbacks below.
 //
 // Block tile BN = WGN * TN * 16 weight rows by BM = WGM * TM * 16 activation
-// rows.  Six waves: four compute waves in a WGN x WGM grid, each owning a
-// (TN * 16) x (TM * 16) tile (per K block it reads TN + TM operand fragments
-// from LDS for TN * TM MFMAs), and two loader waves.  The loaders move each
-// K block's activation rows, weight rows and activation scales with
-// direct-to-LDS loads (global_load_lds: 16 bytes per lane, one 128-byte row
-// per 8 lanes, the lane -> source mapping applying the XOR swizzle) into a
-// ring of STAGES slots, STAGES - 1 blocks ahead, and wait for them with an
-// explicit vmcnt; one bare barrier per K block hands a slot over.  Because
-// vector-memory counters are per wave, the compute waves never wait on the
-// loads in flight (they issue none), and the loaders never stall on LDS
-// reads.  The weight scales of the tile's K range sit in LDS, loaded once.
-constexpr int TK_THREADS = 384;
-
-template <int WGN, int WGM, int TN, int TM, int STAGES, int LAYOUT>
-__global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
+// rows.  Four compute waves in a WGN x WGM grid each own a (TN * 16) x
+// (TM * 16) tile (per K block they read TN + TM operand fragments from LDS
+// for TN * TM MFMAs); NLD loader waves move each K block's activation rows,
+// weight rows and activation scales with direct-to-LDS loads
+// (global_load_lds: 16 bytes per lane, one 128-byte row per 8 lanes, the
+// lane -> source mapping applying the XOR swizzle) into a ring of STAGES
+// slots, STAGES - 1 blocks ahead, and wait for them with an explicit vmcnt;
+// one bare barrier per K block hands a slot over.  Because vector-memory
+// counters are per wave, the compute waves never wait on the loads in flight
+// (they issue none), and the loaders never stall on LDS reads.  The weight
+// scales of the tile's K range sit in LDS, loaded once.
+//
+// Large M (prefill, grouped): 128 x 256 or 256 x 128 tiles, MFMA bound.
+// Small M (decode): the weights are the HBM stream and the output gives few
+// tiles, so the ring is deep (up to 8 slots: the bytes in flight per CU are
+// what sets the bandwidth) and K may be split over `splits` workgroups per
+// output tile.  Each split then writes its fp32 partial tile to a workspace
+// with coherent (sc1) stores, waits for them to land and counts in on a
+// per-tile counter; the last to arrive reads the other partials with
+// coherent loads, adds all of them in split order, rounds to bf16, stores and
+// re-arms the counter.  The result is deterministic, and no agent-wide cache
+// writeback or invalidate is issued (those flush the whole L2 of an XCD).
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, int LAYOUT>
+__global__ __launch_bounds__((4 + NLD) * 64) void tile_kernel(Args a) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   constexpr int ROWS = BM + BN;
   constexpr int SLOT = ROWS * BK + BM * 4;  // operand rows, then the BM activation scales
   constexpr int OCT = ROWS / 8;             // 1 KB row groups per slot
-  constexpr int DMA = OCT / 2;              // row-group loads per loader wave per slot
-  constexpr int SDMA = BM / 128;            // 64-float scale loads per loader wave per slot
-  constexpr int PER_G = DMA + SDMA;         // vector memory instructions per loader per slot
+  constexpr int DMA = OCT / NLD;            // row-group loads per loader wave per slot
+  constexpr int SG = BM / 64;               // 64-float activation-scale loads per slot
+  constexpr int SPL = (SG + NLD - 1) / NLD; // of which per loader (spares repeat one: same bytes, same place)
+  constexpr int PER_G = DMA + SPL;          // vector memory instructions per loader per slot
   constexpr int MAXKB = 160;                // K <= 20480 for the weight-scale preload
-  static_assert(WGN * WGM == 4 && OCT % 2 == 0 && BM % 128 == 0 && 128 % (TN * 16) == 0,
-                "tile shape");
+  constexpr int CT = 256;                   // compute threads
+  static_assert(WGN * WGM == 4 && OCT % NLD == 0 && BM % 64 == 0 && BN % 64 == 0 &&
+                    128 % (TN * 16) == 0, "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ float s_sb[BN > 128 ? 2 : 1][MAXKB];
-  __shared__ int s_group;
+  __shared__ int s_group, s_last;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fg = lane >> 4;
   const int M = a.M, N = a.N, K = a.K, Kb = K / BK, Nb = (N + 127) / 128;
 
-  // tile order: workgroup ids are dealt to the 8 XCDs round robin; give each
-  // XCD a contiguous run of tiles, walked GROUPN weight tiles at a time with
-  // the activation tiles inside, so concurrent tiles on one XCD share panels
+  // work order: workgroup ids are dealt to the 8 XCDs round robin; give each
+  // XCD a contiguous run of (split, tile) items, walked GROUPN weight tiles
+  // at a time with the activation tiles inside, so concurrent tiles on one
+  // XCD share panels
   constexpr int GROUPN = 4;
-  const int T = a.tiles_m * a.tiles_n;
-  int tile = blockIdx.x;
+  const int T = a.tiles_m * a.tiles_n, S = KSPLIT ? a.splits : 1;
+  int item = blockIdx.x;
   {
-    const int x = tile % 8, l = tile / 8, per = T / 8, rem = T % 8;
-    tile = x * per + min(x, rem) + l;
+    const int TS = T * S, x = item % 8, l = item / 8, per = TS / 8, rem = TS % 8;
+    item = x * per + min(x, rem) + l;
   }
+  const int split = item / T, tile = item % T;
   int tn, tm;
   {
     const int gsz = GROUPN * a.tiles_m, grp = tile / gsz, in = tile % gsz;
@@ -315,6 +348,7 @@ __global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
     tm = in / gw;
   }
   const int m0 = tm * BM, n0 = tn * BN;
+  const int kb0 = split * a.kb_per_split, nk = max(0, min(Kb - kb0, a.kb_per_split));
 
   const uint8_t *A = a.A, *B = a.B;
   const float *sa = a.sa, *sb = a.sb;
@@ -344,49 +378,48 @@ __global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
     B += (size_t)g * N * K;
     sb += (size_t)g * Nb * Kb;
   }
-  for (int i = tid; i < (BN > 128 ? 2 : 1) * Kb; i += TK_THREADS) {
-    const int h = i / Kb, kb = i % Kb;
-    s_sb[h][kb] = sb[(size_t)min(n0 / 128 + h, Nb - 1) * Kb + kb];
-  }
-
   if (wave >= 4) {
     // ---------------- loader waves ----------------
     const int L = wave - 4;
-    // q-th row-group load: rows (L + 2q) * 8 .. + 7 of the slot; lane l ->
-    // row + l / 8, physical chunk l % 8 holding logical chunk (l % 8) ^ key(row)
+    // q-th row-group load: rows (L + NLD q) * 8 .. + 7 of the slot; lane l ->
+    // row + l / 8, physical chunk l % 8 holding logical chunk (l % 8) ^ key(row).
+    // Rows past the valid ones re-read the last valid row (never stored).
     uint32_t off[DMA];  // byte offsets from A (rows < BM) or B (the rest); < 2^31
 #pragma unroll
     for (int q = 0; q < DMA; ++q) {
-      const int r = (L + 2 * q) * 8 + (lane >> 3);
+      const int r = (L + NLD * q) * 8 + (lane >> 3);
       const int col = (lane & 7) ^ row_key(r);
-      off[q] = (uint32_t)(r < BM ? min(m0 + r, M - 1) : min(n0 + r - BM, N - 1)) * K + col * 16;
+      off[q] = (uint32_t)(r < BM ? min(m0 + r, mvalid - 1) : min(n0 + r - BM, N - 1)) * K + col * 16;
     }
-    uint32_t soff[SDMA];  // scale floats (L + 2j) * 64 + lane of the tile's rows
+    uint32_t soff[SPL];  // scale floats 64 j + lane of the tile's rows
+    int sdst[SPL];
 #pragma unroll
-    for (int j = 0; j < SDMA; ++j) soff[j] = (uint32_t)min(m0 + (L + 2 * j) * 64 + lane, M - 1);
-    // G(t): K block t (clamped: blocks past the end re-read the last one and
-    // are never consumed) -> slot t % STAGES
+    for (int jj = 0; jj < SPL; ++jj) {
+      const int j = (L + NLD * jj) % SG;
+      soff[jj] = (uint32_t)min(m0 + j * 64 + lane, mvalid - 1);
+      sdst[jj] = ROWS * BK + j * 256;
+    }
+    // G(t): K block kb0 + t (clamped: blocks past the range re-read the last
+    // one and are never consumed) -> slot t % STAGES
 #define TK_G(t)                                                                               \
   do {                                                                                        \
-    const int kb_ = min((t), Kb - 1);                                                         \
+    const int kb_ = kb0 + min((t), nk - 1);                                                   \
     uint8_t *sl_ = lds[(t) % STAGES];                                                         \
     _Pragma("unroll") for (int q = 0; q < DMA; ++q)                                          \
-        dma16(((L + 2 * q) * 8 < BM ? A : B) + off[q] + (uint32_t)kb_ * BK,                   \
-              sl_ + (L + 2 * q) * 1024);                                                      \
-    _Pragma("unroll") for (int j = 0; j < SDMA; ++j)                                          \
-        dma4(sa + soff[j] + (uint32_t)kb_ * M, sl_ + ROWS * BK + (L + 2 * j) * 256);          \
+        dma16(((L + NLD * q) * 8 < BM ? A : B) + off[q] + (uint32_t)kb_ * BK,                 \
+              sl_ + (L + NLD * q) * 1024);                                                    \
+    _Pragma("unroll") for (int jj = 0; jj < SPL; ++jj)                                        \
+        dma4(sa + soff[jj] + (uint32_t)kb_ * M, sl_ + sdst[jj]);                              \
   } while (0)
-    __syncthreads();  // weight scales visible (before any load is in flight: this
-                      // barrier drains the vector-memory queue)
-    if (Kb > 0) {
+    if (nk > 0) {
 #pragma unroll
       for (int t = 0; t < STAGES - 1; ++t) TK_G(t);
     }
-    for (int t0 = 0; t0 < Kb; t0 += STAGES) {
+    for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
       for (int u = 0; u < STAGES; ++u) {
         const int t = t0 + u;
-        if (t >= Kb) break;
+        if (t >= nk) break;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_G * (STAGES - 2)));  // my loads of block t landed
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // ... and everyone's; all compute waves are past block t - 1
@@ -396,6 +429,10 @@ __global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
     }
 #undef TK_G
     __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
+    if (S > 1) {                    // the two barriers of the split-K hand-off
+      __syncthreads();
+      __syncthreads();
+    }
     return;
   }
 
@@ -407,13 +444,19 @@ __global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();  // weight scales visible
+  // the weight scales of the K range go to LDS while the loaders start; the
+  // first K-block barrier publishes them
+  for (int i = tid; i < (BN > 128 ? 2 : 1) * nk; i += CT) {
+    const int h = i / nk, t = i % nk;
+    s_sb[h][t] = sb[(size_t)min(n0 / 128 + h, Nb - 1) * Kb + kb0 + t];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
 
-  for (int t0 = 0; t0 < Kb; t0 += STAGES) {
+  for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
     for (int u = 0; u < STAGES; ++u) {
       const int t = t0 + u;
-      if (t >= Kb) break;
+      if (t >= nk) break;
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();  // block t is in slot u
       asm volatile("" ::: "memory");
@@ -444,6 +487,69 @@ __global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
     }
   }
 
+  if (S > 1) {
+    constexpr int PER = BM * BN;  // floats per partial tile, [(i TM + j) 4 + r][compute thread]
+    float *part = a.ws + (size_t)tile * S * PER;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(part + (size_t)split * PER + (((i * TM + j) * 4 + r) * CT + tid),
+                             acc[i][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before this workgroup counts in
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
+    __syncthreads();
+    if (!s_last) return;
+    // sum in split order.  The other splits' values are fetched GR splits at
+    // a time with coherent (sc1) buffer loads -- plain loads to the compiler,
+    // so they are issued together rather than one round trip each; the own
+    // split and splits past the end use an out-of-range offset (no access).
+    constexpr int V = TN * TM * 4, GR = V >= 96 ? 1 : 96 / V;
+    const __amdgpu_buffer_rsrc_t rp = rsrc(part, (uint32_t)S * PER * 4);
+    float sum[V];
+    for (int s0 = 0; s0 < S; s0 += GR) {
+      float p[GR][V];
+#pragma unroll
+      for (int q = 0; q < GR; ++q) {
+        const int sq = s0 + q;
+        const bool ld = sq < S && sq != split;
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          p[q][v] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(
+                         rp, ld ? (uint32_t)(sq * PER + v * CT + tid) * 4 : OOB, 0, CPOL_SC1));
+      }
+#pragma unroll
+      for (int q = 0; q < GR; ++q) {
+        const int sq = s0 + q;
+        if (sq >= S) break;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int v = (i * TM + j) * 4 + r;
+              const float term = sq == split ? acc[i][j][r] : p[q][v];
+              sum[v] = sq == 0 ? term : sum[v] + term;
+            }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = sum[(i * TM + j) * 4 + r];
+    if (tid == 0)
+      __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int m = m0 + (wm * TM + j) * 16 + fr;
@@ -467,219 +573,6 @@ __global__ __launch_bounds__(TK_THREADS) void tile_kernel(Args a) {
     }
   }
 }
-
-// ---------------------------------------------------------------------------
-// Small-M kernel (decode shapes, M <= 128): the weights are the HBM stream.
-//
-// A workgroup owns MROWS = 16 * MG activation rows, BN = 64 * NBW weight
-// rows and a range of K blocks; wave w owns weight rows [w BN/4, (w+1) BN/4)
-// and all activation rows.  Each K block's activation and weight tiles are
-// read with whole 128-byte rows per 8 lanes (a wave instruction covers 8
-// full lines: the L1 path sustains about 3.5x the bandwidth it gives to
-// MFMA-fragment-shaped requests, which touch 16 half lines each) into a
-// two-slot swizzled LDS ring, staged through registers two blocks ahead;
-// the MFMA fragments are then read from LDS.  Loads past the end of the K
-// range use buffer offsets beyond the resource, which return zeros without
-// touching memory.
-//
-// When the output alone gives too few workgroups to cover the chip, K is
-// also split over `splits` workgroups per output tile: each writes its fp32
-// partial tile to a workspace with coherent (sc1) stores, waits for them to
-// land, and counts in on a per-tile counter; the last to arrive reads the
-// other partials with coherent loads, adds all of them in split order,
-// rounds to bf16, stores, and re-arms the counter.  The result is
-// deterministic, and no agent-wide cache writeback or invalidate is issued
-// (those flush the whole L2 of an XCD).
-struct SkArgs {
-  const uint8_t *A;
-  const float *sa;
-  const uint8_t *B;
-  const float *sb;
-  uint16_t *D;
-  int M, N, K;
-  int splits, kb_per_split;
-  float *ws;
-  unsigned *counters;
-};
-
-constexpr uint32_t OOB = 0x80000000u;  // buffer offset past any resource: reads zeros
-#ifndef SK_RS
-#define SK_RS 2  // register sets: K blocks staged ahead (deeper measured slower on MI355X)
-#endif
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
-}
-
-template <int MG, int NBW, int RS>
-__global__ __launch_bounds__(THREADS) void skinny_kernel(SkArgs a) {
-  constexpr int MROWS = 16 * MG, BN = 64 * NBW;
-  constexpr int U = RS % 2 == 0 ? RS : 2 * RS;  // loop unroll: register set and LDS slot indices static
-  constexpr int CH = (MROWS + BN) * 8 / THREADS;  // 16-byte chunks per thread per K block
-  constexpr int CHA = MROWS * 8 / THREADS;         // of which activation chunks (the first ones)
-  constexpr int SLOT = (MROWS + BN) * BK;
-  static_assert(MROWS * 8 % THREADS == 0 && BN * 8 % THREADS == 0 && 128 % BN == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][SLOT];
-  __shared__ float ssa[2][THREADS];  // sa of the slot's K block; entries >= MROWS unused
-  __shared__ float ssb[2][THREADS];  // sb of the slot's K block, replicated (no ALU on loads
-                                     // before they reach LDS: the compiler would hoist it)
-  __shared__ int s_last;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int fr = lane & 15, fg = lane >> 4;
-  const int ntile = blockIdx.x, split = blockIdx.y, mtile = blockIdx.z;
-  const int n0 = ntile * BN, m0 = mtile * MROWS;
-  const int M = a.M, N = a.N, K = a.K, Kb = K / BK;
-  const int kb0 = split * a.kb_per_split;
-  const int kb1 = min(Kb, kb0 + a.kb_per_split);
-  const int nk = max(kb1 - kb0, 0);
-
-  const __amdgpu_buffer_rsrc_t ra = rsrc(a.A, (uint32_t)M * K);
-  const __amdgpu_buffer_rsrc_t rb = rsrc(a.B, (uint32_t)N * K);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(a.sa, (uint32_t)M * Kb * 4);
-  // chunk i of this thread: row r = c / 8 of the slot (activation rows first), 16-byte column c % 8
-  uint32_t goff[CH];
-  int loff[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = tid + THREADS * i, r = c >> 3, col = c & 7;
-    const int grow = r < MROWS ? min(m0 + r, M - 1) : min(n0 + r - MROWS, N - 1);
-    goff[i] = (uint32_t)grow * K + col * 16;
-    loff[i] = r * BK + chunk_pos(col, r);
-  }
-  const uint32_t soff = (uint32_t)min(m0 + tid, M - 1) * 4;
-  const __amdgpu_buffer_rsrc_t rsb = rsrc(a.sb + (size_t)(n0 / 128) * Kb, (uint32_t)Kb * 4);
-
-  u32x4 st[RS][CH];
-  float sst[RS], sbt[RS];
-  // G(t): global -> registers, K block kb0 + t, register set t % RS (zeros past the range)
-#define SK_G(t)                                                                               \
-  do {                                                                                        \
-    const bool ok_ = (t) < nk;                                                                \
-    const uint32_t ko_ = ok_ ? (uint32_t)(kb0 + (t)) * BK : OOB;                              \
-    sst[(t) % RS] = __builtin_bit_cast(                                                       \
-        float, __builtin_amdgcn_raw_buffer_load_b32(                                          \
-                   rs, ok_ ? soff + (uint32_t)(kb0 + (t)) * M * 4 : OOB, 0, 0));              \
-    sbt[(t) % RS] = __builtin_bit_cast(                                                       \
-        float, __builtin_amdgcn_raw_buffer_load_b32(                                          \
-                   rsb, ok_ ? (uint32_t)(kb0 + (t)) * 4 : OOB, 0, 0));                        \
-    _Pragma("unroll") for (int i = 0; i < CH; ++i) st[(t) % RS][i] = __builtin_bit_cast(     \
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(i < CHA ? ra : rb, goff[i] + ko_, 0, 0)); \
-  } while (0)
-  // W(t): register set t % RS -> LDS slot t & 1
-#define SK_W(t)                                                                               \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < CH; ++i)                                            \
-        *reinterpret_cast<u32x4 *>(&lds[(t) & 1][loff[i]]) = st[(t) % RS][i];                 \
-    ssa[(t) & 1][tid] = sst[(t) % RS];                                                        \
-    ssb[(t) & 1][tid] = sbt[(t) % RS]; /* the same value in every entry */                    \
-  } while (0)
-
-  v4f acc[NBW][MG];
-#pragma unroll
-  for (int j = 0; j < NBW; ++j)
-#pragma unroll
-    for (int i = 0; i < MG; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // Block t: loaded G(t) RS - 1 iterations before it is written to LDS,
-  // W(t) one iteration before it is used.
-#pragma unroll
-  for (int t = 0; t < RS; ++t) SK_G(t);
-  SK_W(0);
-  SK_G(RS);
-  for (int t = 0; t < nk; t += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {  // t % U == 0, so every set / slot index below is static
-      const int tt = t + u;
-      __syncthreads();      // slot tt&1 written; nobody still reads slot (tt+1)&1
-      SK_W(tt + 1);
-      SK_G(tt + 1 + RS);
-      const uint8_t *sl = lds[u & 1];
-      v8i bfr[NBW];
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int row = MROWS + (wave * NBW + j) * 16 + fr;
-        bfr[j] = frag(sl + row * BK, row, fg);
-      }
-#pragma unroll
-      for (int i = 0; i < MG; ++i) {
-        const int row = i * 16 + fr;
-        const v8i afr = frag(sl + row * BK, row, fg);
-        const float s = ssa[u & 1][row] * ssb[u & 1][row];
-        v4f pr[NBW];
-#pragma unroll
-        for (int j = 0; j < NBW; ++j)
-          pr[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bfr[j], afr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int j = 0; j < NBW; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(pr[j][r], s, acc[j][i][r]);
-      }
-    }
-  }
-#undef SK_G
-#undef SK_W
-
-  if (a.splits > 1) {
-    const int tile = mtile * gridDim.x + ntile;
-    constexpr int PER = THREADS * NBW * MG * 4;  // floats per partial tile
-    float *part = a.ws + (size_t)tile * a.splits * PER;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-#pragma unroll
-      for (int i = 0; i < MG; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __hip_atomic_store(part + (size_t)split * PER + (((j * MG + i) * 4 + r) * THREADS + tid),
-                             acc[j][i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before this workgroup counts in
-    __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.splits - 1);
-    __syncthreads();
-    if (!s_last) return;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-#pragma unroll
-      for (int i = 0; i < MG; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float t = 0.f;
-          for (int s = 0; s < a.splits; ++s)
-            t += s == split ? acc[j][i][r]
-                            : __hip_atomic_load(
-                                  part + (size_t)s * PER + (((j * MG + i) * 4 + r) * THREADS + tid),
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          acc[j][i][r] = t;
-        }
-    if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-#pragma unroll
-  for (int i = 0; i < MG; ++i) {
-    const int m = m0 + i * 16 + fr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int n = n0 + (wave * NBW + j) * 16 + 4 * fg;
-      uint16_t *dp = a.D + (size_t)m * N + n;
-      const uint32_t b0 = bf16_bits(acc[j][i][0]), b1 = bf16_bits(acc[j][i][1]);
-      const uint32_t b2 = bf16_bits(acc[j][i][2]), b3 = bf16_bits(acc[j][i][3]);
-      if ((N & 3) == 0 && n + 3 < N) {
-        *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-      } else {
-        if (n < N) dp[0] = (uint16_t)b0;
-        if (n + 1 < N) dp[1] = (uint16_t)b1;
-        if (n + 2 < N) dp[2] = (uint16_t)b2;
-        if (n + 3 < N) dp[3] = (uint16_t)b3;
-      }
-    }
-  }
-}
-
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ---- split-K workspace: one per (device, stream), made on first need ------
@@ -716,45 +609,69 @@ const Workspace *workspace(hipStream_t s) {
   return &(g_ws[{dev, s}] = w);
 }
 
-// Optional override for tuning sweeps: FP8GEMM_SKINNY="nbw,splits" (nbw: 16-row
-// weight groups per wave, 1 or 2).
-bool skinny_override(int *nbw, int *splits) {
-  const char *e = getenv("FP8GEMM_SKINNY");
-  return e && sscanf(e, "%d,%d", nbw, splits) == 2 && (*nbw == 1 || *nbw == 2) && *splits >= 1;
-}
-
-template <int MG, int NBW>
-int launch_skinny(SkArgs a, int m_tiles, int n_tiles, hipStream_t stream) {
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool KSPLIT = false>
+int launch_tile(Args a, int groups, hipStream_t stream) {
+  a.tiles_m = cdiv(a.M, WGM * TM * 16);
+  a.tiles_n = cdiv(a.N, WGN * TN * 16);
+  if (!KSPLIT) {
+    a.splits = 1;
+    a.kb_per_split = a.K / BK;
+  }
   void *kargs[] = {&a};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&skinny_kernel<MG, NBW, SK_RS>),
-                                 dim3(n_tiles, a.splits, m_tiles), dim3(THREADS), kargs, 0, stream);
+  hipError_t e = hipLaunchKernel(
+      reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, KSPLIT, LAYOUT>),
+      dim3(a.tiles_m * a.tiles_n * a.splits, groups), dim3((4 + NLD) * 64), kargs, 0, stream);
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
-// Dense GEMM with at most 128 activation rows per m-tile.
-int run_skinny(const uint8_t *A, const float *sa, const uint8_t *B, const float *sb, uint16_t *D,
-               int M, int N, int K, hipStream_t stream) {
-  const int MG = M <= 64 ? 4 : 8;
-  const int m_tiles = cdiv(M, 16 * MG);
-  const int Kb = K / BK;
-  int nbw = 1, splits = 1;
-  if (!skinny_override(&nbw, &splits)) {
-    // measured on MI355X (decode shapes, weights streamed from HBM): one
-    // 16-row weight group per wave; a two-way K split pays for its partial
-    // exchange only when there are few output tiles
-    nbw = 1;
-    const int tiles = cdiv(N, 64) * m_tiles;
-    splits = tiles < 100 ? 2 : 1;
-  }
-  const int n_tiles = cdiv(N, 64 * nbw);
-  splits = std::max(1, std::min(splits, std::max(Kb, 1)));
+// Dense GEMM with M <= 128 (decode): the tile kernel with a deep ring, four
+// loader waves, 64 weight rows per tile and a K split sized so that the
+// (split, tile) items cover the chip.
+// Optional override for tuning sweeps: FP8GEMM_DECODE="bn,stages,splits".
+struct DecodeCfg {
+  int bn, stages, splits;
+};
+
+// Instances built: (bn, stages) in {(64,4), (64,6), (128,4)} for both
+// activation tile heights.
+bool decode_built(int bn, int stages, int bm) {
+  (void)bm;
+  return (bn == 64 && (stages == 4 || stages == 6)) || (bn == 128 && stages == 4);
+}
+
+// Default (measured on MI355X over the decode shapes, weights streamed from
+// HBM): four slots; 64 weight rows per tile unless the output alone gives
+// 384 or more such tiles, then 128 (fewer activation re-reads per weight
+// byte); a K split only when the tiles alone leave CUs idle, and at most one
+// split per 14 K blocks, since the partial hand-off costs about 2-3 us.
+DecodeCfg decode_config(int M, int N, int K) {
+  const int bm = M <= 64 ? 64 : 128;
+  const char *e = getenv("FP8GEMM_DECODE");
+  DecodeCfg o;
+  if (e && sscanf(e, "%d,%d,%d", &o.bn, &o.stages, &o.splits) == 3 && o.splits >= 1 &&
+      decode_built(o.bn, o.stages, bm))
+    return o;
+  const int Kb = K / BK, tiles64 = cdiv(N, 64);
+  DecodeCfg c{tiles64 >= 384 ? 128 : 64, 4, 1};
+  const int tiles = cdiv(N, c.bn) * cdiv(M, bm);
+  c.splits = std::max(1, std::min(256 / std::max(tiles, 1), Kb / 14));
+  return c;
+}
+
+int run_decode(Args a, hipStream_t stream) {
+  DecodeCfg c = decode_config(a.M, a.N, a.K);
+  const int Kb = a.K / BK;
+  const int bm = a.M <= 64 ? 64 : 128;
+  int splits = std::max(1, std::min(c.splits, std::max(Kb, 1)));
   const int kps = Kb > 0 ? cdiv(Kb, splits) : 0;
   splits = Kb > 0 ? cdiv(Kb, kps) : 1;
-  SkArgs a{A, sa, B, sb, D, M, N, K, splits, kps, nullptr, nullptr};
+  a.splits = splits;
+  a.kb_per_split = kps;
   if (splits > 1) {
+    const int tiles = cdiv(a.N, c.bn) * cdiv(a.M, bm);
     const Workspace *w = workspace(stream);
-    const size_t need = (size_t)n_tiles * m_tiles * splits * 16 * MG * 64 * nbw;
-    if (!w || need > WS_FLOATS || n_tiles * m_tiles > WS_COUNTERS) {
+    const size_t need = (size_t)tiles * splits * bm * c.bn;
+    if (!w || need > WS_FLOATS || tiles > WS_COUNTERS) {
       a.splits = 1;
       a.kb_per_split = Kb;
     } else {
@@ -762,22 +679,15 @@ int run_skinny(const uint8_t *A, const float *sa, const uint8_t *B, const float 
       a.counters = w->counters;
     }
   }
-  if (MG == 4)
-    return nbw == 2 ? launch_skinny<4, 2>(a, m_tiles, n_tiles, stream)
-                    : launch_skinny<4, 1>(a, m_tiles, n_tiles, stream);
-  return nbw == 2 ? launch_skinny<8, 2>(a, m_tiles, n_tiles, stream)
-                  : launch_skinny<8, 1>(a, m_tiles, n_tiles, stream);
-}
-
-template <int WGN, int WGM, int TN, int TM, int STAGES, int LAYOUT>
-int launch_tile(Args a, int groups, hipStream_t stream) {
-  a.tiles_m = cdiv(a.M, WGM * TM * 16);
-  a.tiles_n = cdiv(a.N, WGN * TN * 16);
-  void *kargs[] = {&a};
-  hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, LAYOUT>),
-      dim3(a.tiles_m * a.tiles_n, groups), dim3(TK_THREADS), kargs, 0, stream);
-  return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+#define DEC(BN_, ST_)                                                                  \
+  if (c.bn == BN_ && c.stages == ST_)                                                  \
+    return bm == 64 ? launch_tile<1, 4, BN_ / 16, 1, ST_, 4, DENSE, true>(a, 1, stream) \
+                    : launch_tile<1, 4, BN_ / 16, 2, ST_, 4, DENSE, true>(a, 1, stream);
+  DEC(64, 4)
+  DEC(64, 6)
+  DEC(128, 4)
+#undef DEC
+  return FP8GEMM_LAUNCH_FAILED;  // unreachable: decode_config returns built instances only
 }
 
 template <int BM, int BN, int LAYOUT>
@@ -818,12 +728,11 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
                               (long long)M * N);
   if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
-         static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0};
+         static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, K / BK, nullptr, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= 128)
-    return run_skinny(a.A, sa, a.B, sb, a.D, M, N, K, s);
+  if (M <= 128 && K <= 20480) return run_decode(a, s);
   if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
-  return launch_tile<2, 2, 4, 8, 3, DENSE>(a, 1, s);
+  return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -836,9 +745,9 @@ int grouped_contiguous(const void *A, const float *sa, const void *B, const floa
   if (!aligned(m_indices, 4)) return FP8GEMM_MISALIGNED;
   if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
-         static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0};
+         static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0, 1, K / BK, nullptr, nullptr};
   if (K > 20480) return launch<128, 128, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
-  return launch_tile<4, 1, 4, 8, 3, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
+  return launch_tile<4, 1, 4, 8, 3, 2, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
 }
 
 int grouped_masked(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -852,10 +761,10 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   if (!aligned(masked_m, 4)) return FP8GEMM_MISALIGNED;
   if (G > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
-         static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0};
+         static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0, 1, K / BK, nullptr, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (expected_m <= 64 || K > 20480) return launch<64, 128, MASKED>(a, G, s);
-  return launch_tile<2, 2, 4, 8, 3, MASKED>(a, G, s);
+  return launch_tile<2, 2, 4, 8, 3, 2, MASKED>(a, G, s);
 }
 
 const char *fp8gemm_status_string(int status) {

@@ -167,6 +167,66 @@ def test_decode_workload_sampled(M, N, K):
     assert_close(out[pm, pn], ref, f"decode {M}x{N}x{K}")
 
 
+# K-split / ring-depth / tile-width variants of the small-M path, chosen
+# through the library's tuning override; every variant must meet the bar on
+# the whole output (ragged K ranges: 15 blocks over 2, 3, 4, 7 and 15 splits)
+DECODE_VARIANTS = [("FP8GEMM_DECODE", v) for v in
+                   ("64,4,1", "64,6,2", "64,6,7", "128,4,3", "64,4,15", "128,4,1", "64,4,4")]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 640), (64, 2112, 1920), (100, 300, 1920),
+                                   (128, 2112, 1920)])
+def test_decode_variants_full(M, N, K, monkeypatch):
+    seed = 1500 + M + N
+    d = W.dense(seed, M, N, K)
+    ref = oracle.gemm(d["A"], d["sa"], d["B"], d["sb"])
+    outs = []
+    for var, val in DECODE_VARIANTS:
+        announce(f"decode variant {var}={val} {M}x{N}x{K} seed {seed}")
+        monkeypatch.setenv(var, val)
+        outs.append(gpu_dense(d))
+        monkeypatch.delenv(var)
+        assert_close(outs[-1], ref, f"{var}={val} {M}x{N}x{K}")
+    # the split-K sum runs in split order: a repeated call is bitwise identical
+    monkeypatch.setenv("FP8GEMM_DECODE", "64,6,7")
+    assert (gpu_dense(d) == outs[2]).all()
+    monkeypatch.delenv("FP8GEMM_DECODE")
+
+
+def test_decode_graph_replay():
+    """Captured split-K launches: every replay equals the eager result (the
+    arrival counters are re-armed by the kernel, no memset in the graph)."""
+    M, N, K = 128, 2112, 7168
+    d = W.dense(1600, M, N, K)
+    A, sa, B, sb = to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"])
+    s = torch.cuda.Stream()
+    D = sentinel_out((M, N))
+    torch.cuda.synchronize()
+    announce("decode graph replay 128x2112x7168")
+    with torch.cuda.stream(s):
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)  # eager: makes the stream's workspace
+    s.synchronize()
+    eager = bits(D)
+    g = torch.cuda.CUDAGraph()
+    D2 = sentinel_out((M, N))
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D2)
+    for r in range(3):
+        D2.fill_(0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        assert (bits(D2) == eager).all(), f"replay {r}"
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)  # eager work between replays
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(1600)
+    pm, pn = sample_points(rng, M, N, 2000)
+    ref = oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn)
+    assert_close(eager[pm, pn], ref, "graph replay")
+
+
 @pytest.mark.parametrize("M,N,K", W.PREFILL_SHAPES)
 def test_prefill_workload_sampled(M, N, K):
     seed = 3000 + W.PREFILL_SHAPES.index((M, N, K))
