@@ -118,7 +118,14 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM: copy a MIB-sized buffer 5 times (a plain copy "
                          "kernel of known size, used to calibrate rocprofv3 byte counters)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="no GPU: turn the rocprofv3 outputs of the profiling commands (see "
+                         "profile_commands) under DIR into profiles/<workload>.md and "
+                         "profiles/<workload>.traffic.json")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU form "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
@@ -245,6 +252,130 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def profile_commands(workload, out="gpurun_out/prof"):
+    """The rocprofv3 runs a profile summary is built from (run from the
+    repository root after `cd /tmp && export TMPDIR=/tmp`)."""
+    w = workload
+    b = f"python3 bench.py --workload {w} --no-cpu-baseline"
+    return [
+        ("kt", f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/{w}/kt -o {w} -- {b} --steps 20 --warmup 5"),
+        ("fetch", f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/{w}/fetch -o {w} -- {b} --steps 2 --warmup 1"),
+        ("write", f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/{w}/write -o {w} -- {b} --steps 2 --warmup 1"),
+        ("cfetch", f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/copy/fetch -o copy -- python3 bench.py --copy-probe 1024"),
+        ("cwrite", f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/copy/write -o copy -- python3 bench.py --copy-probe 1024"),
+    ]
+
+
+def _ours(name):
+    return "tile_kernel" in name or "gemm_kernel" in name
+
+
+def _call_of_dispatches(n, line):
+    """Map the i-th library dispatch of a bench run to its call index, from the
+    bench's fixed launch order: eager pass over every rotation copy, warm-up
+    and timed graph replays (all calls in order), then per call (reps + 1)
+    replays of a graph holding `copies` launches of that call."""
+    nc, copies = len(line["per_call"]), line["config"]["rotating_copies"]
+    reps = max(3, min(50, line["steps"] // 4))
+    head = nc * (copies + line["warmup"] + line["steps"])
+    tail = nc * (reps + 1) * copies
+    if n != head + tail:
+        raise SystemExit(f"profile has {n} library dispatches, bench order implies {head + tail}")
+    return [i % nc if i < head else (i - head) // ((reps + 1) * copies) for i in range(n)]
+
+
+def _last_json(path):
+    for ln in reversed(open(path).read().splitlines()):
+        if ln.startswith("{"):
+            return json.loads(ln)
+    raise SystemExit(f"no JSON line in {path}")
+
+
+def summarize_profile(d, workload):
+    import csv
+    import glob
+    import hashlib
+    import statistics as st
+    w = workload
+    src = os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc", "fp8gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+
+    def rows(pattern):
+        f = glob.glob(os.path.join(d, pattern))
+        if len(f) != 1:
+            raise SystemExit(f"expected one file for {pattern}, found {f}")
+        return list(csv.DictReader(open(f[0])))
+
+    kt = sorted((r for r in rows(f"{w}/kt/*kernel_trace.csv") if _ours(r["Kernel_Name"])),
+                key=lambda r: int(r["Dispatch_Id"]))
+    kline = _last_json(os.path.join(d, w, "kt.log"))
+    kcall = _call_of_dispatches(len(kt), kline)
+    labels = [c["call"] for c in kline["per_call"]]
+
+    def counter(sub):
+        rs = sorted((r for r in rows(f"{w}/{sub}/*counter_collection.csv") if _ours(r["Kernel_Name"])),
+                    key=lambda r: int(r["Dispatch_Id"]))
+        line = _last_json(os.path.join(d, w, f"{sub}.log"))
+        cc = _call_of_dispatches(len(rs), line)
+        out = {}
+        for r, c in zip(rs, cc):
+            out.setdefault(c, []).append(float(r["Counter_Value"]) * 1024)
+        return out
+
+    def copy_scale(sub, name):
+        rs = [r for r in rows(f"copy/{sub}/*counter_collection.csv") if "copyBuffer" in r["Kernel_Name"]]
+        kib = st.mean(float(r["Counter_Value"]) for r in rs)
+        return (1 << 30) / (kib * 1024), kib
+
+    fscale, fkib = copy_scale("fetch", "FETCH_SIZE")
+    wscale, wkib = copy_scale("write", "WRITE_SIZE")
+    fetch, write = counter("fetch"), counter("write")
+    table, traffic = [], {}
+    for i, lab in enumerate(labels):
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000 for r, c in zip(kt, kcall) if c == i]
+        r0 = next(r for r, c in zip(kt, kcall) if c == i)
+        import re
+        m = re.search(r"(tile_kernel|gemm_kernel)<[^>]*>", r0["Kernel_Name"])
+        name = m.group(0) if m else r0["Kernel_Name"]
+        grid = (int(r0["Grid_Size_X"]) // int(r0["Workgroup_Size_X"]), int(r0["Grid_Size_Y"]))
+        fb = st.mean(fetch[i]) * fscale
+        wb = st.mean(write[i]) * wscale
+        alg = kline["per_call"][i]["bytes"]
+        traffic[lab] = {"fetch_bytes": fb, "write_bytes": wb}
+        table.append(f"| {lab} | `{name}` | {grid[0]},{grid[1]} | {len(durs)} | {st.mean(durs):.2f} | "
+                     f"{st.median(durs):.2f} | {min(durs):.2f} | {kline['per_call'][i]['avg_us']:.2f} | "
+                     f"{fb / 1e6:.2f} | {wb / 1e6:.2f} | {alg / 1e6:.2f} | {(fb + wb) / alg:.2f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    cmds = "\n".join(f"    {c}" for _, c in profile_commands(w))
+    md = f"""# rocprofv3: {w} workload
+
+Workload: {WORKLOAD_TEXT[w]}; seeded synthetic inputs, {kline['config']['rotating_copies']} rotating
+input copies (> 1 GB) so the weights come from HBM.  Kernel source sha256 `{sha}`
+(moe_grouped_gemm_act_amd/csrc/fp8gemm.hip).
+
+Commands (repository root, one MI355X, after `cd /tmp && export TMPDIR=/tmp`), then
+`python3 bench.py --workload {w} --summarize-profile gpurun_out/prof` to write this file:
+
+{cmds}
+
+Per call: kernel trace durations (all dispatches of that call in the traced bench run), the
+bench's own HIP-event average for the same call in that run, and HBM bytes per dispatch from
+the two counter runs, scaled by the copy calibration below.  "ratio" = measured HBM bytes /
+algorithmic bytes (A, B, scales and D once each).
+
+| call | kernel | grid (x,y) | launches | avg us | median us | min us | bench avg us | FETCH (MB) | WRITE (MB) | algorithmic (MB) | ratio |
+|---|---|---|---|---|---|---|---|---|---|---|---|
+""" + "\n".join(table) + f"""
+
+Calibration: a 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE {fkib:.0f} KiB and
+WRITE_SIZE {wkib:.0f} KiB per dispatch: scale factors {fscale:.3f} (fetch) and {wscale:.3f} (write).
+"""
+    open(os.path.join(ROOT, "profiles", f"{w}.md"), "w").write(md)
+    json.dump({"source_sha256": sha, "fetch_scale": fscale, "write_scale": wscale, "kernels": traffic},
+              open(os.path.join(ROOT, "profiles", f"{w}.traffic.json"), "w"), indent=1)
+    print(md)
 
 
 def measured_traffic(kernel):

@@ -255,16 +255,6 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Args a) {
   }
 }
 
-// Direct-to-LDS loads (global_load_lds): each lane's `bytes` from global
-// memory land at lds + lane * bytes.  Kept in a device function: written in a
-// kernel template, the builtin makes the host pass drop the kernel's stub.
-__device__ __forceinline__ void dma16(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *g, void *lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
-}
-
 // Buffer resource over [p, p + bytes): raw buffer loads past the end return
 // zeros without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
@@ -272,6 +262,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
 }
 constexpr int CPOL_SC1 = 16;  // buffer cache-policy bit: device-coherent access (sc1)
 constexpr uint32_t OOB = 0x80000000u;  // buffer offset past any resource: reads zeros
+
+// Direct-to-LDS buffer loads (buffer_load ... lds): each lane's `bytes` at
+// byte offset `off` of the resource land at lds + lane * bytes; an offset
+// past the resource writes zeros and moves no data.  Kept in device
+// functions: written in a kernel template, the builtin makes the host pass
+// drop the kernel's stub.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, void *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4,
+                                           off, 0, 0, 0);
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (vmcnt: bits 3:0 and 15:14; expcnt and lgkmcnt
@@ -305,7 +309,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F
 // re-arms the counter.  The result is deterministic, and no agent-wide cache
 // writeback or invalidate is issued (those flush the whole L2 of an XCD).
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, int LAYOUT>
-__global__ __launch_bounds__((4 + NLD) * 64) void tile_kernel(Args a) {
+__global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   constexpr int ROWS = BM + BN;
   constexpr int SLOT = ROWS * BK + BM * 4;  // operand rows, then the BM activation scales
@@ -315,8 +319,9 @@ __global__ __launch_bounds__((4 + NLD) * 64) void tile_kernel(Args a) {
   constexpr int SPL = (SG + NLD - 1) / NLD; // of which per loader (spares repeat one: same bytes, same place)
   constexpr int PER_G = DMA + SPL;          // vector memory instructions per loader per slot
   constexpr int MAXKB = 160;                // K <= 20480 for the weight-scale preload
-  constexpr int CT = 256;                   // compute threads
-  static_assert(WGN * WGM == 4 && OCT % NLD == 0 && BM % 64 == 0 && BN % 64 == 0 &&
+  constexpr int NCW = WGN * WGM;            // compute waves
+  constexpr int CT = NCW * 64;              // compute threads
+  static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 64 == 0 &&
                     128 % (TN * 16) == 0, "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
@@ -378,25 +383,34 @@ __global__ __launch_bounds__((4 + NLD) * 64) void tile_kernel(Args a) {
     B += (size_t)g * N * K;
     sb += (size_t)g * Nb * Kb;
   }
-  if (wave >= 4) {
+  if (wave >= NCW) {
     // ---------------- loader waves ----------------
-    const int L = wave - 4;
+    const int L = wave - NCW;
+    constexpr int QA = BM / 8 / NLD;  // loads q < QA are activation row groups, the rest weights
+    static_assert((BM / 8) % NLD == 0, "row groups split evenly between A and B");
+    const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint32_t)M * K);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(B, (uint32_t)N * K);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(sa, (uint32_t)M * Kb * 4);
     // q-th row-group load: rows (L + NLD q) * 8 .. + 7 of the slot; lane l ->
     // row + l / 8, physical chunk l % 8 holding logical chunk (l % 8) ^ key(row).
-    // Rows past the valid ones re-read the last valid row (never stored).
-    uint32_t off[DMA];  // byte offsets from A (rows < BM) or B (the rest); < 2^31
+    // Rows past the valid ones (activation rows >= mvalid, weight rows >= N)
+    // read out of range: zeros, no memory traffic; they are never stored.
+    uint32_t off[DMA];  // byte offsets into A (q < QA) or B
 #pragma unroll
     for (int q = 0; q < DMA; ++q) {
       const int r = (L + NLD * q) * 8 + (lane >> 3);
       const int col = (lane & 7) ^ row_key(r);
-      off[q] = (uint32_t)(r < BM ? min(m0 + r, mvalid - 1) : min(n0 + r - BM, N - 1)) * K + col * 16;
+      if (q < QA)
+        off[q] = m0 + r < mvalid ? (uint32_t)(m0 + r) * K + col * 16 : OOB;
+      else
+        off[q] = n0 + r - BM < N ? (uint32_t)(n0 + r - BM) * K + col * 16 : OOB;
     }
-    uint32_t soff[SPL];  // scale floats 64 j + lane of the tile's rows
+    uint32_t soff[SPL];  // byte offsets of scale floats 64 j + lane of the tile's rows
     int sdst[SPL];
 #pragma unroll
     for (int jj = 0; jj < SPL; ++jj) {
       const int j = (L + NLD * jj) % SG;
-      soff[jj] = (uint32_t)min(m0 + j * 64 + lane, mvalid - 1);
+      soff[jj] = m0 + j * 64 + lane < mvalid ? (uint32_t)(m0 + j * 64 + lane) * 4 : OOB;
       sdst[jj] = ROWS * BK + j * 256;
     }
     // G(t): K block kb0 + t (clamped: blocks past the range re-read the last
@@ -406,10 +420,9 @@ __global__ __launch_bounds__((4 + NLD) * 64) void tile_kernel(Args a) {
     const int kb_ = kb0 + min((t), nk - 1);                                                   \
     uint8_t *sl_ = lds[(t) % STAGES];                                                         \
     _Pragma("unroll") for (int q = 0; q < DMA; ++q)                                          \
-        dma16(((L + NLD * q) * 8 < BM ? A : B) + off[q] + (uint32_t)kb_ * BK,                 \
-              sl_ + (L + NLD * q) * 1024);                                                    \
+        dma16(q < QA ? ra : rb, off[q] + (uint32_t)kb_ * BK, sl_ + (L + NLD * q) * 1024);     \
     _Pragma("unroll") for (int jj = 0; jj < SPL; ++jj)                                        \
-        dma4(sa + soff[jj] + (uint32_t)kb_ * M, sl_ + sdst[jj]);                              \
+        dma4(rs, soff[jj] + (uint32_t)kb_ * M * 4, sl_ + sdst[jj]);                           \
   } while (0)
     if (nk > 0) {
 #pragma unroll
@@ -620,7 +633,8 @@ int launch_tile(Args a, int groups, hipStream_t stream) {
   void *kargs[] = {&a};
   hipError_t e = hipLaunchKernel(
       reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, KSPLIT, LAYOUT>),
-      dim3(a.tiles_m * a.tiles_n * a.splits, groups), dim3((4 + NLD) * 64), kargs, 0, stream);
+      dim3(a.tiles_m * a.tiles_n * a.splits, groups), dim3((WGN * WGM + NLD) * 64), kargs, 0,
+      stream);
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
@@ -732,7 +746,12 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= 128 && K <= 20480) return run_decode(a, s);
   if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
-  return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
+  // 256 activation rows x 128 weight rows, eight compute waves (two per
+  // SIMD, so one wave's promotion FMAs run under the other's MFMAs) and four
+  // loader waves; FP8GEMM_LARGE=6 selects the four-compute-wave layout
+  const char *e = getenv("FP8GEMM_LARGE");
+  if (e && e[0] == '6') return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
+  return launch_tile<2, 4, 4, 4, 3, 4, DENSE>(a, 1, s);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -747,7 +766,12 @@ int grouped_contiguous(const void *A, const float *sa, const void *B, const floa
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0, 1, K / BK, nullptr, nullptr};
   if (K > 20480) return launch<128, 128, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
-  return launch_tile<4, 1, 4, 8, 3, 2, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
+  // 256 weight rows x 128 activation rows (one expert per 128-row block),
+  // eight compute waves and four loader waves
+  const char *e = getenv("FP8GEMM_LARGE");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (e && e[0] == '6') return launch_tile<4, 1, 4, 8, 3, 2, CONTIG>(a, 1, s);
+  return launch_tile<4, 2, 4, 4, 3, 4, CONTIG>(a, 1, s);
 }
 
 int grouped_masked(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -763,8 +787,12 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0, 1, K / BK, nullptr, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (expected_m <= 64 || K > 20480) return launch<64, 128, MASKED>(a, G, s);
-  return launch_tile<2, 2, 4, 8, 3, 2, MASKED>(a, G, s);
+  if (K > 20480) return launch<64, 128, MASKED>(a, G, s);
+  // measured on MI355X (G = 16, 256-row capacity, counts ~ U[0, 256]):
+  // 128 weight rows by 128 activation rows, four loader waves, four slots;
+  // 64-row activation tiles when the hint says counts are small
+  if (expected_m <= 64) return launch_tile<1, 4, 8, 1, 4, 4, MASKED>(a, G, s);
+  return launch_tile<1, 4, 8, 2, 4, 4, MASKED>(a, G, s);
 }
 
 const char *fp8gemm_status_string(int status) {

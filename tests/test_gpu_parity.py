@@ -257,6 +257,29 @@ def test_contiguous_small_full():
     assert_close(out[~pad], ref[~pad], "contiguous small")
 
 
+@pytest.mark.parametrize("variant", ["default", "6"])
+def test_large_tile_variants_full(variant, monkeypatch):
+    """The large-M tile kernel's wave layouts (eight compute waves, the
+    default; four compute and two loader waves through the tuning override)
+    on dense and contiguous problems spanning several tiles and ragged edges."""
+    if variant != "default":
+        monkeypatch.setenv("FP8GEMM_LARGE", variant)
+    for (M, N, K) in ((300, 520, 640), (512, 2112, 1024)):
+        seed = 1700 + M + N
+        announce(f"large variant {variant} dense {M}x{N}x{K} seed {seed}")
+        d = W.dense(seed, M, N, K)
+        assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]),
+                     f"variant {variant} {M}x{N}x{K}")
+    d = W.contiguous(4150, 3, 128 * 7, 300, 512, uniform=False)
+    announce(f"large variant {variant} contiguous G=3 896x300x512")
+    out = gpu_contig(d)
+    ref = oracle.grouped_contiguous(d["A"], d["sa"], d["B"], d["sb"], d["m_indices"],
+                                    np.full((d["M"], d["N"]), SENTINEL, np.uint16))
+    pad = d["m_indices"] < 0
+    assert (out[pad] == SENTINEL).all() and (out[~pad] != SENTINEL).all()
+    assert_close(out[~pad], ref[~pad], f"variant {variant} contiguous")
+
+
 def test_contiguous_edge_cases():
     G, N, K, M = 4, 200, 256, 128 * 6
     idx = np.full(M, -1, np.int32)
