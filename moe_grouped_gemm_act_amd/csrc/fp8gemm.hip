@@ -72,12 +72,14 @@ struct Args {
 };
 
 // XOR key of an LDS row: 16-byte chunk c of row r sits at position
-// c ^ key(r).  Rows r and r+1 share a 256-byte bank window and rows r, r+8
-// share banks; this key makes any 8 consecutive rows, and the 8 even / 8 odd
-// rows of a 16-row fragment, hit distinct chunks.  It depends on r mod 16
-// only, so every 16-row fragment of a tile has the same per-lane pattern and
-// the compiler can address all of them from one base with immediate offsets.
-__device__ __forceinline__ int row_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// c ^ key(r).  A fragment read has lane l at row base + l % 16, chunk l / 16
+// (and + 4); with key(r) = (r >> 1) & 7 these ds_read_b128 accesses are free
+// of bank conflicts on gfx950 (measured with the SQ_LDS_BANK_CONFLICT
+// counter: zero, against half of all LDS cycles for a key that separates
+// only rows 8 apart).  It depends on r mod 16 only, so every 16-row fragment
+// of a tile has the same per-lane pattern and the compiler can address all
+// of them from one base with immediate offsets.
+__device__ __forceinline__ int row_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int chunk_pos(int chunk, int row) { return (chunk ^ row_key(row)) << 4; }
 
 // fp32 -> bf16 bits, round to nearest even; NaN -> canonical quiet NaN
@@ -465,6 +467,19 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
+  // Product k = j * TN + i of a K block (activation group j, weight group i)
+  // comes from one MFMA; it is promoted LAG MFMAs later, when it has long
+  // landed, so the promotion FMAs issue in the shadow of the next MFMAs
+  // instead of waiting on the one just issued.  Products sit in a ring of
+  // RING registers; TN * TM is a multiple of RING, so slots and the promotion
+  // of the previous block's last products line up across blocks.  The next
+  // activation fragment and its scale are read from LDS one group ahead.
+  constexpr int LAG = 2, RING = 4;
+  static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
+  v4f ring[RING];
+#pragma unroll
+  for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
+  float sc_last = 0.f;  // scale of the previous block's last activation group
   for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
     for (int u = 0; u < STAGES; ++u) {
@@ -476,29 +491,47 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
       const uint8_t *sl = lds[u];
       const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
       const float sbv = s_sb[hsb][t];
-      v8i bfr[TN];
+      v8i bfr[TN], afr[2];
+      float scb[TM];
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int row = BM + (wn * TN + i) * 16 + fr;
         bfr[i] = frag(sl + row * BK, row, fg);
       }
+      {
+        const int row = wm * TM * 16 + fr;
+        afr[0] = frag(sl + row * BK, row, fg);
+        scb[0] = ssl[row] * sbv;
+      }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const int row = (wm * TM + j) * 16 + fr;
-        const v8i afr = frag(sl + row * BK, row, fg);
-        const float sc = ssl[row] * sbv;
-        v4f pr[TN];
+        if (j + 1 < TM) {
+          const int row = (wm * TM + j + 1) * 16 + fr;
+          afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
+          scb[j + 1] = ssl[row] * sbv;
+        }
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
-          pr[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bfr[i], afr, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        for (int i = 0; i < TN; ++i) {
+          const int k = j * TN + i;
+          ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          const int kp = k - LAG;                      // product promoted now
+          const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
+          const float sp = kp >= 0 ? scb[kq / TN] : sc_last;
+          v4f &ap = acc[kq % TN][kq / TN];
+          const v4f &pp = ring[(kq + RING) % RING];
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[i][r], sc, acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) ap[r] = __builtin_fmaf(pp[r], sp, ap[r]);
+        }
       }
+      sc_last = scb[TM - 1];
     }
   }
+#pragma unroll
+  for (int k = TN * TM - LAG; k < TN * TM; ++k)  // the last block's last products
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
 
   if (S > 1) {
     constexpr int PER = BM * BN;  // floats per partial tile, [(i TM + j) 4 + r][compute thread]
