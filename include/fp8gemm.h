@@ -32,8 +32,9 @@
  *    enqueued.  No call synchronises or reads device memory on the host, so
  *    every call may be captured into a HIP graph.
  *  - Library-owned memory: the dense call with M <= 128 may split K over
- *    several workgroups and then needs a workspace (64 MB of fp32 partial
- *    tiles and 256 KB of arrival counters).  It is allocated with hipMalloc
+ *    several workgroups; it then enqueues two kernels (partial products,
+ *    then their sum in a fixed order, so results are deterministic) and
+ *    needs a workspace of 64 MB for the fp32 partials.  It is allocated with hipMalloc
  *    the first time a call on a given (device, stream) needs it, kept until
  *    the process ends, and never allocated while the stream is capturing: a
  *    call made during capture before the stream has a workspace runs

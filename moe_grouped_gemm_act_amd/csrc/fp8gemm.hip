@@ -67,8 +67,7 @@ struct Args {
   const int32_t *idx;  // m_indices (CONTIG) or masked_m (MASKED)
   int tiles_m, tiles_n;
   int splits, kb_per_split;  // K split over workgroups (tile kernel, dense only); 1 and K/128 otherwise
-  float *ws;                 // split-K partial tiles and arrival counters (splits > 1)
-  unsigned *counters;
+  float *ws;                 // split-K partial planes [splits][M][N] (splits > 1)
 };
 
 // XOR key of an LDS row: 16-byte chunk c of row r sits at position
@@ -262,7 +261,6 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Args a) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
 }
-constexpr int CPOL_SC1 = 16;  // buffer cache-policy bit: device-coherent access (sc1)
 constexpr uint32_t OOB = 0x80000000u;  // buffer offset past any resource: reads zeros
 
 // Direct-to-LDS buffer loads (buffer_load ... lds): each lane's `bytes` at
@@ -302,14 +300,11 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F
 //
 // Large M (prefill, grouped): 128 x 256 or 256 x 128 tiles, MFMA bound.
 // Small M (decode): the weights are the HBM stream and the output gives few
-// tiles, so the ring is deep (up to 8 slots: the bytes in flight per CU are
-// what sets the bandwidth) and K may be split over `splits` workgroups per
-// output tile.  Each split then writes its fp32 partial tile to a workspace
-// with coherent (sc1) stores, waits for them to land and counts in on a
-// per-tile counter; the last to arrive reads the other partials with
-// coherent loads, adds all of them in split order, rounds to bf16, stores and
-// re-arms the counter.  The result is deterministic, and no agent-wide cache
-// writeback or invalidate is issued (those flush the whole L2 of an XCD).
+// tiles, so K may be split over `splits` workgroups per output tile.  Each
+// split then writes its fp32 partial tile to its own plane of a workspace
+// and ends; splitk_reduce_kernel, launched next on the same stream, adds the
+// planes in split order and rounds to bf16, spread over the whole chip.  The
+// result is deterministic, and nothing waits on another workgroup.
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, int LAYOUT>
 __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
@@ -328,7 +323,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ float s_sb[BN > 128 ? 2 : 1][MAXKB];
-  __shared__ int s_group, s_last;
+  __shared__ int s_group;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,10 +439,6 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     }
 #undef TK_G
     __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
-    if (S > 1) {                    // the two barriers of the split-K hand-off
-      __syncthreads();
-      __syncthreads();
-    }
     return;
   }
 
@@ -534,66 +525,26 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
       acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
 
   if (S > 1) {
-    constexpr int PER = BM * BN;  // floats per partial tile, [(i TM + j) 4 + r][compute thread]
-    float *part = a.ws + (size_t)tile * S * PER;
+    // this split's fp32 partial goes to its own [M][N] plane of the
+    // workspace; splitk_reduce_kernel (next on the stream) sums the planes
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + (wm * TM + j) * 16 + fr;
+      if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
+      for (int i = 0; i < TN; ++i) {
+        const int n = n0 + (wn * TN + i) * 16 + 4 * fg;
+        float *pp = a.ws + ((size_t)split * M + m) * N + n;
+        if ((N & 3) == 0 && n + 3 < N) {
+          *reinterpret_cast<v4f *>(pp) = acc[i][j];
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __hip_atomic_store(part + (size_t)split * PER + (((i * TM + j) * 4 + r) * CT + tid),
-                             acc[i][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // the partial has landed before this workgroup counts in
-    __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
-    __syncthreads();
-    if (!s_last) return;
-    // sum in split order.  The other splits' values are fetched GR splits at
-    // a time with coherent (sc1) buffer loads -- plain loads to the compiler,
-    // so they are issued together rather than one round trip each; the own
-    // split and splits past the end use an out-of-range offset (no access).
-    constexpr int V = TN * TM * 4, GR = V >= 96 ? 1 : 96 / V;
-    const __amdgpu_buffer_rsrc_t rp = rsrc(part, (uint32_t)S * PER * 4);
-    float sum[V];
-    for (int s0 = 0; s0 < S; s0 += GR) {
-      float p[GR][V];
-#pragma unroll
-      for (int q = 0; q < GR; ++q) {
-        const int sq = s0 + q;
-        const bool ld = sq < S && sq != split;
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-          p[q][v] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(
-                         rp, ld ? (uint32_t)(sq * PER + v * CT + tid) * 4 : OOB, 0, CPOL_SC1));
-      }
-#pragma unroll
-      for (int q = 0; q < GR; ++q) {
-        const int sq = s0 + q;
-        if (sq >= S) break;
-#pragma unroll
-        for (int i = 0; i < TN; ++i)
-#pragma unroll
-          for (int j = 0; j < TM; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int v = (i * TM + j) * 4 + r;
-              const float term = sq == split ? acc[i][j][r] : p[q][v];
-              sum[v] = sq == 0 ? term : sum[v] + term;
-            }
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) pp[r] = acc[i][j][r];
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = sum[(i * TM + j) * 4 + r];
-    if (tid == 0)
-      __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
 
 #pragma unroll
@@ -619,18 +570,65 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     }
   }
 }
+// Split-K reduction (decode): D[m][n] = bf16(sum over s, in split order, of
+// ws[s][m][n]).  One thread per 4 consecutive columns of a row; the planes
+// are fetched 8 at a time with buffer loads (planes past S read out of range:
+// zeros, no traffic) so the loads of one thread are issued together.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, uint16_t *D, int M,
+                                                            int N, int S) {
+  const int nq = (N + 3) / 4;
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (long long)M * nq) return;
+  const int m = (int)(q / nq), n = (int)(q % nq) * 4;
+  const uint32_t plane = (uint32_t)M * N * 4;
+  const __amdgpu_buffer_rsrc_t r = rsrc(ws, plane * (uint32_t)S);
+  const bool vec = (N & 3) == 0;
+  const uint32_t off = ((uint32_t)m * N + n) * 4;
+  v4f sum = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    v4f p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t o = s0 + k < S ? off + (uint32_t)(s0 + k) * plane : OOB;
+      if (vec) {
+        p[k] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p[k][e] = n + e < N ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                              r, o == OOB ? OOB : o + 4 * e, 0, 0))
+                              : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k >= S) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] = s0 + k == 0 ? p[k][e] : sum[e] + p[k][e];
+    }
+  }
+  uint16_t *dp = D + (size_t)m * N + n;
+  const uint32_t b0 = bf16_bits(sum[0]), b1 = bf16_bits(sum[1]);
+  const uint32_t b2 = bf16_bits(sum[2]), b3 = bf16_bits(sum[3]);
+  if (vec) {
+    *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+  } else {
+    if (n < N) dp[0] = (uint16_t)b0;
+    if (n + 1 < N) dp[1] = (uint16_t)b1;
+    if (n + 2 < N) dp[2] = (uint16_t)b2;
+    if (n + 3 < N) dp[3] = (uint16_t)b3;
+  }
+}
+
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ---- split-K workspace: one per (device, stream), made on first need ------
-// Holds fp32 partial tiles and per-tile arrival counters (zeroed once here,
-// re-armed by the kernels).  Never allocated while the stream is capturing:
-// such calls run without a K split instead.
+// Holds the fp32 partial planes of a split call.  Never allocated while the
+// stream is capturing: such calls run without a K split instead.
 constexpr size_t WS_FLOATS = size_t(16) << 20;  // 64 MB of partials
-constexpr int WS_COUNTERS = 1 << 16;
 
 struct Workspace {
   float *part = nullptr;
-  unsigned *counters = nullptr;
 };
 
 std::mutex g_ws_mu;
@@ -647,11 +645,6 @@ const Workspace *workspace(hipStream_t s) {
   Workspace w;
   if (hipMalloc(reinterpret_cast<void **>(&w.part), WS_FLOATS * sizeof(float)) != hipSuccess)
     return nullptr;
-  if (hipMalloc(reinterpret_cast<void **>(&w.counters), WS_COUNTERS * sizeof(unsigned)) != hipSuccess ||
-      hipMemsetAsync(w.counters, 0, WS_COUNTERS * sizeof(unsigned), s) != hipSuccess) {
-    (void)hipFree(w.part);
-    return nullptr;
-  }
   return &(g_ws[{dev, s}] = w);
 }
 
@@ -689,8 +682,9 @@ bool decode_built(int bn, int stages, int bm) {
 // Default (measured on MI355X over the decode shapes, weights streamed from
 // HBM): four slots; 64 weight rows per tile unless the output alone gives
 // 384 or more such tiles, then 128 (fewer activation re-reads per weight
-// byte); a K split only when the tiles alone leave CUs idle, and at most one
-// split per 14 K blocks, since the partial hand-off costs about 2-3 us.
+// byte); a K split only when the tiles alone leave CUs idle, with (tiles x
+// splits) kept within one wave of 256 workgroups and at least 9 K blocks per
+// split, since the partial planes and their reduction cost about 3 us.
 DecodeCfg decode_config(int M, int N, int K) {
   const int bm = M <= 64 ? 64 : 128;
   const char *e = getenv("FP8GEMM_DECODE");
@@ -701,7 +695,7 @@ DecodeCfg decode_config(int M, int N, int K) {
   const int Kb = K / BK, tiles64 = cdiv(N, 64);
   DecodeCfg c{tiles64 >= 384 ? 128 : 64, 4, 1};
   const int tiles = cdiv(N, c.bn) * cdiv(M, bm);
-  c.splits = std::max(1, std::min(256 / std::max(tiles, 1), Kb / 14));
+  c.splits = std::max(1, std::min(256 / std::max(tiles, 1), Kb / 9));
   return c;
 }
 
@@ -715,26 +709,28 @@ int run_decode(Args a, hipStream_t stream) {
   a.splits = splits;
   a.kb_per_split = kps;
   if (splits > 1) {
-    const int tiles = cdiv(a.N, c.bn) * cdiv(a.M, bm);
     const Workspace *w = workspace(stream);
-    const size_t need = (size_t)tiles * splits * bm * c.bn;
-    if (!w || need > WS_FLOATS || tiles > WS_COUNTERS) {
+    if (!w || (size_t)splits * a.M * a.N > WS_FLOATS) {
       a.splits = 1;
       a.kb_per_split = Kb;
     } else {
       a.ws = w->part;
-      a.counters = w->counters;
     }
   }
-#define DEC(BN_, ST_)                                                                  \
-  if (c.bn == BN_ && c.stages == ST_)                                                  \
-    return bm == 64 ? launch_tile<1, 4, BN_ / 16, 1, ST_, 4, DENSE, true>(a, 1, stream) \
-                    : launch_tile<1, 4, BN_ / 16, 2, ST_, 4, DENSE, true>(a, 1, stream);
+  int st = FP8GEMM_LAUNCH_FAILED;  // unreachable: decode_config returns built instances only
+#define DEC(BN_, ST_)                                                                     \
+  if (c.bn == BN_ && c.stages == ST_)                                                     \
+    st = bm == 64 ? launch_tile<1, 4, BN_ / 16, 1, ST_, 4, DENSE, true>(a, 1, stream)      \
+                  : launch_tile<1, 4, BN_ / 16, 2, ST_, 4, DENSE, true>(a, 1, stream);
   DEC(64, 4)
   DEC(64, 6)
   DEC(128, 4)
 #undef DEC
-  return FP8GEMM_LAUNCH_FAILED;  // unreachable: decode_config returns built instances only
+  if (st != FP8GEMM_OK || a.splits == 1) return st;
+  const long long quads = (long long)a.M * cdiv(a.N, 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                     stream, a.ws, a.D, a.M, a.N, a.splits);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
 template <int BM, int BN, int LAYOUT>
@@ -775,7 +771,7 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
                               (long long)M * N);
   if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
-         static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, K / BK, nullptr, nullptr};
+         static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, K / BK, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= 128 && K <= 20480) return run_decode(a, s);
   if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
@@ -797,7 +793,7 @@ int grouped_contiguous(const void *A, const float *sa, const void *B, const floa
   if (!aligned(m_indices, 4)) return FP8GEMM_MISALIGNED;
   if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
-         static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0, 1, K / BK, nullptr, nullptr};
+         static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0, 1, K / BK, nullptr};
   if (K > 20480) return launch<128, 128, CONTIG>(a, 1, static_cast<hipStream_t>(stream));
   // 256 weight rows x 128 activation rows (one expert per 128-row block),
   // eight compute waves and four loader waves
@@ -818,7 +814,7 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   if (!aligned(masked_m, 4)) return FP8GEMM_MISALIGNED;
   if (G > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
-         static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0, 1, K / BK, nullptr, nullptr};
+         static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0, 1, K / BK, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K > 20480) return launch<64, 128, MASKED>(a, G, s);
   // measured on MI355X (G = 16, 256-row capacity, counts ~ U[0, 256]):
