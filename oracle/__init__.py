@@ -44,6 +44,10 @@ def _bind(lib):
     lib.fp8ref_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32]
     lib.fp8ref_grouped_contiguous.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32]
     lib.fp8ref_grouped_masked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32]
+    lib.fp8ref_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.fp8ref_e4m3_encode.restype = ctypes.c_uint8
+    lib.fp8ref_quantize_1x128.argtypes = [vp, i32, i32, vp, vp]
+    lib.fp8ref_quantize_1x128.restype = i32
     lib.fp8ref_points.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp,
                                   vp, vp, vp]
     for f in (lib.fp8ref_gemm, lib.fp8ref_grouped_contiguous, lib.fp8ref_grouped_masked,
@@ -165,3 +169,22 @@ def points(kind, A, sa, B, sb, pm, pn, pg=None, m_indices=None, want64=False, li
 def bf16_bits_to_float(bits):
     """bf16 bit patterns (uint16) -> float32 values (exact widening)."""
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_encode(v, lib=None):
+    """Nearest e4m3fn code to the fp32 value v (ties to the even code,
+    saturating at 448, NaN to the NaN code)."""
+    return int((lib or load()).fp8ref_e4m3_encode(float(np.float32(v))))
+
+
+def quantize_1x128(x_bf16_bits, lib=None):
+    """x: uint16 bf16 bits [M, K] -> (codes uint8 [M, K], sa float32 [K/128, M])."""
+    x = _c(x_bf16_bits, np.uint16)
+    M, K = x.shape
+    codes = np.empty((M, K), np.uint8)
+    sa = np.empty((K // 128, M), np.float32)
+    rc = (lib or load()).fp8ref_quantize_1x128(_p(x), M, K, _p(codes), _p(sa))
+    if rc:
+        raise ValueError("fp8ref_quantize_1x128: bad shape")
+    return codes, sa
+

@@ -278,3 +278,68 @@ int fp8ref_points(int kind, const uint8_t *A, const float *sa, const uint8_t *B,
   }
   return 0;
 }
+
+/* ---- 1x128 activation quantisation (the step before the GEMM) ----------
+ * The pages leave the FP8 conversion of activations to the caller (kakushin,
+ * "Hvorfor FP8 og FP4 er interessant": scales, rounding and layout have to be
+ * handled right for low precision to work).  With the 1x128 granularity this
+ * library reads, each 128-wide K block x of a row gets one fp32 scale
+ *   s = amax|x| / 448   (fp32 division; 1 when the block is all zero;
+ *                        NaN elements do not take part in the maximum)
+ * and codes e4m3(x / s), the division in fp32 and the encoding to the
+ * nearest e4m3fn value.  Input is bf16 bits [M][K]; codes are [M][K], scales
+ * are stored K-block-major, sa[kb][m], as the GEMM reads them. */
+
+/* Nearest e4m3fn code to v, written as the definition: a search over the
+ * finite codes of v's sign; a tie goes to the even code (mantissa LSB 0);
+ * magnitudes past 448 take 448 (the largest finite value); NaN gives the
+ * NaN code of its sign. */
+uint8_t fp8ref_e4m3_encode(float v) {
+  if (isnan(v)) return signbit(v) ? 0xFF : 0x7F;
+  const double *d = dec();
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs((double)v);
+  int best = 0;
+  double bestd = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    const double diff = fabs(d[c] - a);
+#if MUTANT == 7 /* planted mistake: ties go to the larger code */
+    if (diff < bestd || diff == bestd) {
+#else
+    if (diff < bestd || (diff == bestd && (c & 1) == 0)) {
+#endif
+      best = c;
+      bestd = diff;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+static float bf16_to_float(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+int fp8ref_quantize_1x128(const uint16_t *x, int M, int K, uint8_t *codes, float *sa) {
+  if (M < 0 || K < 0 || K % 128 != 0) return 1;
+  const int Kb = K / 128;
+  for (long m = 0; m < M; ++m)
+    for (int kb = 0; kb < Kb; ++kb) {
+      const uint16_t *xb = x + m * (long)K + kb * 128;
+      float amax = 0.0f;
+      for (int k = 0; k < 128; ++k) {
+        const float a = fabsf(bf16_to_float(xb[k]));
+        if (a > amax) amax = a; /* false for NaN: NaN is skipped */
+      }
+#if MUTANT == 8 /* planted mistake: scale amax / 447 */
+      const float s = amax == 0.0f ? 1.0f : amax / 447.0f;
+#else
+      const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+#endif
+      sa[(long)kb * M + m] = s;
+      for (int k = 0; k < 128; ++k) codes[m * (long)K + kb * 128 + k] = fp8ref_e4m3_encode(bf16_to_float(xb[k]) / s);
+    }
+  return 0;
+}

@@ -401,6 +401,87 @@ def test_empty_problems():
     assert (D == 0).all()
 
 
+# ------------------------------------------- 1x128 activation quantiser ----
+
+
+def torch_e4m3_bits(v):
+    """PyTorch's own float32 -> float8_e4m3fn conversion (round to nearest
+    even; callers keep |v| below the overflow threshold)."""
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def bf16_of(x):
+    """float32 array -> bf16 bits (round to nearest even) and its exact value"""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16), t.to(torch.float32).numpy()
+
+
+def test_e4m3_encode_round_trips_every_code():
+    for c in FINITE:
+        assert oracle.e4m3_encode(TV[c]) == c if not (c == 0x80) else oracle.e4m3_encode(-0.0) == 0x80
+
+
+def test_e4m3_encode_ties_go_to_even():
+    pos = [c for c in FINITE if c < 0x7F]
+    for c in pos[:-1]:
+        mid = (TV[c] + TV[c + 1]) / 2  # exact in fp32
+        assert np.float32(mid) == mid
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == even, hex(c)
+        assert oracle.e4m3_encode(-mid) == even | 0x80
+
+
+def test_e4m3_encode_matches_torch():
+    rng = np.random.default_rng(31)
+    mag = 2.0 ** rng.uniform(-12, np.log2(448), 20000)
+    v = (mag * rng.choice([-1, 1], mag.size)).astype(np.float32)
+    got = np.array([oracle.e4m3_encode(x) for x in v], np.uint8)
+    assert (got == torch_e4m3_bits(v)).all()
+
+
+def test_e4m3_encode_saturates_and_nan():
+    for v in (448.0, 449.0, 463.99, 464.0, 1e6, float("inf")):
+        assert oracle.e4m3_encode(v) == 0x7E and oracle.e4m3_encode(-v) == 0xFE
+    assert oracle.e4m3_encode(float("nan")) in (0x7F, 0xFF)
+
+
+def test_quantize_1x128_definition():
+    rng = np.random.default_rng(32)
+    M, K = 6, 512
+    xb, x = bf16_of(rng.standard_normal((M, K)).astype(np.float32) * 3)
+    x[2, 128:256] = 0.0
+    xb[2, 128:256] = 0  # an all-zero block
+    xb[4, 10] = np.uint16(0x7FC0)  # a NaN element (skipped by the maximum)
+    x[4, 10] = np.nan
+    codes, sa = oracle.quantize_1x128(xb)
+    for m in range(M):
+        for kb in range(K // 128):
+            blk = x[m, kb * 128:(kb + 1) * 128]
+            amax = np.float32(np.nanmax(np.abs(blk)))
+            s = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(448.0))
+            assert sa[kb, m] == s
+            q = (blk / s).astype(np.float32)
+            ok = ~np.isnan(q)
+            assert (codes[m, kb * 128:(kb + 1) * 128][ok] == torch_e4m3_bits(q[ok])).all()
+            assert (codes[m, kb * 128:(kb + 1) * 128][~ok] & 0x7F == 0x7F).all()
+            if amax > 0:  # the block's largest magnitude lands on +-448
+                j = int(np.nanargmax(np.abs(blk)))
+                assert codes[m, kb * 128 + j] & 0x7F == 0x7E
+    assert (sa[1, 2] == 1.0) and (codes[2, 128:256] == 0).all()
+
+
+def test_quantize_1x128_error_bound():
+    rng = np.random.default_rng(33)
+    xb, x = bf16_of((rng.standard_normal((8, 1024)) * np.exp(rng.uniform(-8, 8, (8, 1)))).astype(np.float32))
+    codes, sa = oracle.quantize_1x128(xb)
+    deq = TV[codes] * np.repeat(sa.T, 128, axis=1)
+    # normal e4m3 values carry 3 fraction bits: half a step is 2^-4 relative;
+    # below 2^-6 (in units of the scale) the step is 2^-9
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, np.repeat(sa.T, 128, axis=1) * 2.0 ** -10)
+    assert (np.abs(deq - x) <= bound * (1 + 1e-6)).all()
+
+
 # ------------------------------------------------------ planted mistakes ----
 
 MUTANTS = {
@@ -410,6 +491,8 @@ MUTANTS = {
     4: "rounds to bf16 through binary32 (double rounding)",
     5: "computes padding rows of the contiguous layout with expert 0",
     6: "pairs output column n with weight row n^1",
+    7: "rounds e4m3 ties towards the larger code",
+    8: "quantises with scale amax / 447",
 }
 
 
@@ -437,6 +520,15 @@ def _pins_pass(lib):
                                   lib=lib)
     if not (D[100:] == 0x7FBF).all():
         failed.append("padding_untouched")
+    # e4m3 tie: halfway between 1.0 (0x38) and 1.125 (0x39) goes to the even code
+    if oracle.e4m3_encode(1.0625, lib=lib) != 0x38:
+        failed.append("e4m3_tie")
+    # quantiser scale: a block whose largest magnitude is 896 has scale exactly 2
+    xb = np.zeros((1, 128), np.uint16)
+    xb[0, 5] = np.uint16(0x4460)  # bf16 896.0
+    codes, sa = oracle.quantize_1x128(xb, lib=lib)
+    if sa[0, 0] != 2.0 or codes[0, 5] != 0x7E:
+        failed.append("quantise_scale")
     return failed
 
 
