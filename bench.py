@@ -55,6 +55,11 @@ class Call:
         self.kind, self.d, self.label, self.flop, self.bytes = kind, d, label, flop, by
 
     def to_device(self, torch, dev):
+        if self.kind == "quant":
+            X = torch.from_numpy(self.d["X"].view("int16")).view(torch.bfloat16).to(dev)
+            M, K = self.d["M"], self.d["K"]
+            return {"X": X, "A": torch.empty((M, K), dtype=torch.uint8, device=dev),
+                    "sa": torch.empty((K // 128, M), dtype=torch.float32, device=dev)}
         keys = ["A", "sa", "B", "sb"] + (["m_indices"] if self.kind == "contiguous" else []) \
             + (["masked_m"] if self.kind == "masked" else [])
         t = {k: torch.from_numpy(self.d[k]).to(dev) for k in keys}
@@ -63,7 +68,9 @@ class Call:
         return t
 
     def launch(self, fg, t):
-        if self.kind == "dense":
+        if self.kind == "quant":
+            fg.quantize_fp8_1x128(t["X"], t["A"], t["sa"])
+        elif self.kind == "dense":
             fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
         elif self.kind == "contiguous":
             fg.grouped_contiguous(t["A"], t["sa"], t["B"], t["sb"], t["m_indices"], t["D"])
@@ -87,6 +94,15 @@ def workload_calls(name):
             counts = np.bincount(d["m_indices"][d["m_indices"] >= 0], minlength=G)
             flop, by = grouped_cost(counts.tolist(), N, K)
             calls.append(Call("contiguous", d, f"contiguous G={G} {rows}x{N}x{K}", flop, by + 4 * rows))
+    elif name == "quant":
+        import torch
+        import synth
+        for i, (M, N, K) in enumerate(W.PREFILL_SHAPES):
+            x = synth.normal(6000 + i, M * K).reshape(M, K)
+            x[synth.heavy_rows(6007 + i, M) > 1] *= 50
+            xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            d = {"X": xb, "M": M, "K": K}
+            calls.append(Call("quant", d, f"quantize {M}x{K}", 0.0, 3 * M * K + 4 * M * (K // 128)))
     elif name == "masked":
         for i, (G, M, N, K) in enumerate(W.MASKED_CASES):
             d = W.masked(5000 + i, G, M, N, K)
@@ -103,8 +119,9 @@ WORKLOAD_TEXT = {
     "small": "dense FP8 GEMM 128x256x512",
     "contiguous": "MoE grouped FP8 GEMM, M-axis contiguous: G=4 x 8192 rows and G=8 uneven (32768 padded rows), N=4096, K=7168",
     "masked": "MoE grouped FP8 GEMM, masked: G=16, 256 rows/expert, masked_m ~ U[0,256], (N,K) in {(4096,7168),(7168,2048)}",
+    "quant": "1x128 FP8 quantisation of bf16 activations, M=4096 x K in {16384,7168,1536,18432} (the prefill A operands), 1% rows x50",
 }
-MEMORY_BOUND = {"decode", "small", "masked"}
+MEMORY_BOUND = {"decode", "small", "masked", "quant"}
 
 
 def main():
@@ -254,6 +271,16 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def source_sha256():
+    """sha256 over the library's kernel sources (csrc/*.hip, in name order)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc", "*.hip"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def profile_commands(workload, out="gpurun_out/prof"):
     """The rocprofv3 runs a profile summary is built from (run from the
     repository root after `cd /tmp && export TMPDIR=/tmp`)."""
@@ -296,11 +323,9 @@ def _last_json(path):
 def summarize_profile(d, workload):
     import csv
     import glob
-    import hashlib
     import statistics as st
     w = workload
-    src = os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc", "fp8gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = source_sha256()
 
     def rows(pattern):
         f = glob.glob(os.path.join(d, pattern))
@@ -353,7 +378,7 @@ def summarize_profile(d, workload):
 
 Workload: {WORKLOAD_TEXT[w]}; seeded synthetic inputs, {kline['config']['rotating_copies']} rotating
 input copies (> 1 GB) so the weights come from HBM.  Kernel source sha256 `{sha}`
-(moe_grouped_gemm_act_amd/csrc/fp8gemm.hip).
+(moe_grouped_gemm_act_amd/csrc/*.hip, in name order).
 
 Commands (repository root, one MI355X, after `cd /tmp && export TMPDIR=/tmp`), then
 `python3 bench.py --workload {w} --summarize-profile gpurun_out/prof` to write this file:
@@ -383,9 +408,7 @@ def measured_traffic(kernel):
     `kernel`, from the committed profile summaries -- only when they were taken
     on the kernel source as it is now; otherwise None."""
     import glob
-    import hashlib
-    src = os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc", "fp8gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = source_sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.json"))):
         d = json.load(open(f))
         k = d.get("kernels", {}).get(kernel)
@@ -408,6 +431,17 @@ def cpu_baseline(calls, budget_s, memory_bound):
     while True:
         for c in calls:
             d = c.d
+            if c.kind == "quant":
+                M, K = d["X"].shape
+                left = max(0.2, budget_s - (time.perf_counter() - t0))
+                rows = max(1, min(M, int(left * 2e6 / K)))  # the oracle encodes ~2e6 values/s
+                oracle.quantize_1x128(np.ascontiguousarray(d["X"][:rows]))
+                if passes == 0:
+                    done.append(f"quantize {rows}x{K}")
+                by += 3 * rows * K + 4 * rows * (K // 128)
+                if time.perf_counter() - t0 > budget_s:
+                    break
+                continue
             A, sa, B, sb = d["A"], d["sa"], d["B"], d["sb"]
             if c.kind == "masked":
                 A, sa, B, sb = A[0], sa[0], B[0], sb[0]
@@ -431,7 +465,9 @@ def cpu_baseline(calls, budget_s, memory_bound):
             break
     dt = time.perf_counter() - t0
     val = by / dt / 1e9 if memory_bound else fl / dt / 1e12
-    return {"value": val, "unit": "GB/s" if memory_bound else "TFLOP/s", "cores": threads,
+    # the oracle's GEMM runs on `threads` host threads, its quantiser on one
+    cores = 1 if all(c.kind == "quant" for c in calls) else threads
+    return {"value": val, "unit": "GB/s" if memory_bound else "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": dt, "gflops": fl / dt / 1e9,
             "sample": f"{passes} pass(es) over whole output rows of each call (first pass: "
                       + ", ".join(done) + f"), stopped after about {budget_s:.0f} s"}

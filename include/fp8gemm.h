@@ -109,6 +109,26 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
                    int M, int N, int K, int G, void *stream, const int32_t *masked_m,
                    int expected_m);
 
+/*
+ * 1x128 activation quantisation: the FP8 conversion the pages leave to the
+ * caller (kakushin.no, "Hvorfor FP8 og FP4 er interessant"), producing the A
+ * and sa operands of the calls above.
+ *   X [M,K] bf16 bits (device, read); A [M,K] e4m3fn codes (device, written);
+ *   sa [K/128][M] fp32 (device, written; M contiguous as the GEMM reads it).
+ *   For each row m and 128-wide K block x:
+ *     s = amax|x| / 448 (IEEE fp32 division; 1 for an all-zero block; NaN
+ *         elements take no part in the maximum),
+ *     A = the e4m3fn value nearest to x / s (IEEE fp32 division), ties to the
+ *         even code, magnitudes past 448 saturating to 448, NaN to the NaN
+ *         code; the sign bit of every code is the sign of x (so -0 stays
+ *         -0, and an infinite element, whose block scale is infinite, gives
+ *         the NaN code of its own sign).
+ * Constraints: K % 128 == 0; X and A 16-byte aligned, sa 4-byte aligned;
+ * M * K * 2 < 2^31.  M == 0 or K == 0 returns FP8GEMM_OK without launching.
+ * Allocates nothing; asynchronous on `stream` like the calls above.
+ */
+int quantize_fp8_1x128(const void *X, void *A, float *sa, int M, int K, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8gemm_status_string(int status);
 

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8gemm.h")
 
 __all__ = ["gemm_fp8_1x128_128x128_bf16", "grouped_contiguous", "grouped_masked",
-           "fp8gemm_status_string", "Fp8GemmError", "load_library", "LIB_PATH"]
+           "quantize_fp8_1x128", "fp8gemm_status_string", "Fp8GemmError", "load_library",
+           "LIB_PATH"]
 
 
 class Fp8GemmError(RuntimeError):
@@ -47,7 +48,9 @@ def load_library():
         lib.gemm_fp8_1x128_128x128_bf16.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
         lib.grouped_contiguous.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
         lib.grouped_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32]
-        for f in (lib.gemm_fp8_1x128_128x128_bf16, lib.grouped_contiguous, lib.grouped_masked):
+        lib.quantize_fp8_1x128.argtypes = [vp, vp, vp, i32, i32, vp]
+        for f in (lib.gemm_fp8_1x128_128x128_bf16, lib.grouped_contiguous, lib.grouped_masked,
+                  lib.quantize_fp8_1x128):
             f.restype = i32
         lib.fp8gemm_status_string.argtypes = [i32]
         lib.fp8gemm_status_string.restype = ctypes.c_char_p
@@ -165,3 +168,23 @@ def grouped_masked(A, sa, B, sb, masked_m, expected_m, D=None, stream=None):
         _p(A), _p(sa), _p(B), _p(sb), _p(D), M, N, K, G, _stream(stream, dev), _p(masked_m),
         int(expected_m)))
     return D
+
+
+def quantize_fp8_1x128(X, A=None, sa=None, stream=None):
+    """1x128 quantisation of bf16 activations X [M,K]: returns (A [M,K] e4m3fn
+    codes as uint8, sa [K/128,M] float32), the operands of the GEMM calls."""
+    M, K = X.shape
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    if A is None:
+        A = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    if sa is None:
+        sa = torch.empty((K // 128, M), dtype=torch.float32, device=X.device)
+    A = _codes(A, "A")
+    _shape(A, (M, K), "A")
+    _shape(sa, (K // 128, M), "sa")
+    if sa.dtype != torch.float32:
+        raise TypeError("sa must be float32")
+    dev = _dev(X, A, sa)
+    _check(load_library().quantize_fp8_1x128(_p(X), _p(A), _p(sa), M, K, _stream(stream, dev)))
+    return A, sa

@@ -4,7 +4,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fp8gemm.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("fp8gemm.hip", "quant.hip")]
 LIB = os.path.join(HERE, "libfp8gemm.so")
 
 FLAGS = [
@@ -16,7 +16,7 @@ FLAGS = [
 
 
 def command(out=LIB, extra=()):
-    return ["hipcc", *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", out, SRC]
+    return ["hipcc", *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", out, *SRCS]
 
 
 def build(out=LIB, extra=()):

@@ -287,8 +287,9 @@ int fp8ref_points(int kind, const uint8_t *A, const float *sa, const uint8_t *B,
  *   s = amax|x| / 448   (fp32 division; 1 when the block is all zero;
  *                        NaN elements do not take part in the maximum)
  * and codes e4m3(x / s), the division in fp32 and the encoding to the
- * nearest e4m3fn value.  Input is bf16 bits [M][K]; codes are [M][K], scales
- * are stored K-block-major, sa[kb][m], as the GEMM reads them. */
+ * nearest e4m3fn value, the code's sign being x's.  Input is bf16 bits
+ * [M][K]; codes are [M][K], scales are stored K-block-major, sa[kb][m], as
+ * the GEMM reads them. */
 
 /* Nearest e4m3fn code to v, written as the definition: a search over the
  * finite codes of v's sign; a tie goes to the even code (mantissa LSB 0);
@@ -339,7 +340,14 @@ int fp8ref_quantize_1x128(const uint16_t *x, int M, int K, uint8_t *codes, float
       const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
 #endif
       sa[(long)kb * M + m] = s;
-      for (int k = 0; k < 128; ++k) codes[m * (long)K + kb * 128 + k] = fp8ref_e4m3_encode(bf16_to_float(xb[k]) / s);
+      /* the code's sign is x's: that is the quotient's sign for any s > 0,
+       * and it also fixes the sign of the NaN an infinite element gives
+       * (inf / inf), which IEEE arithmetic leaves open */
+      for (int k = 0; k < 128; ++k) {
+        const float xk = bf16_to_float(xb[k]);
+        codes[m * (long)K + kb * 128 + k] =
+            (uint8_t)(fp8ref_e4m3_encode(fabsf(xk / s)) | (signbit(xk) ? 0x80 : 0x00));
+      }
     }
   return 0;
 }

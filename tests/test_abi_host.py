@@ -21,7 +21,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = fg.declared_functions()
     assert set(names) == {"gemm_fp8_1x128_128x128_bf16", "grouped_contiguous",
-                          "grouped_masked", "fp8gemm_status_string"}
+                          "grouped_masked", "quantize_fp8_1x128", "fp8gemm_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -75,6 +75,20 @@ def test_masked_validation(lib):
     assert call(K=130) == SHAPE
     assert call(G=1 << 16, M=1, K=128) == SHAPE
     assert lib.grouped_masked(NUL, NUL, NUL, NUL, NUL, 0, 64, 128, 4, NUL, NUL, 0) == OK
+
+
+def test_quantize_validation(lib):
+    def call(X=P, A=P, sa=P, M=64, K=256):
+        return lib.quantize_fp8_1x128(X, A, sa, M, K, NUL)
+    assert call(M=-1) == INVALID
+    assert call(X=NUL) == INVALID
+    assert call(sa=NUL) == INVALID
+    assert call(K=130) == SHAPE
+    assert call(M=1 << 20, K=1 << 12) == SHAPE  # M * K * 2 past 2^31
+    assert call(X=P_ODD) == MISALIGNED
+    assert call(A=P_ODD) == MISALIGNED
+    assert call(sa=ctypes.c_void_p(0x10002)) == MISALIGNED
+    assert call(X=NUL, A=NUL, sa=NUL, M=0) == OK  # empty: nothing launched
 
 
 def test_binding_rejects_bad_tensors():
