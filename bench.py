@@ -295,8 +295,24 @@ def profile_commands(workload, out="gpurun_out/prof"):
     ]
 
 
+_PRIMARY = ("tile_kernel", "gemm_kernel", "quant_kernel")
+_FOLLOWER = ("splitk_reduce_kernel",)  # runs right after its call's tile kernel
+
+
 def _ours(name):
-    return "tile_kernel" in name or "gemm_kernel" in name
+    return any(k in name for k in _PRIMARY + _FOLLOWER)
+
+
+def _launches(rows):
+    """Group library dispatches (in dispatch order) into call launches: each
+    primary kernel plus the split-K reduction that follows it, if any."""
+    out = []
+    for r in rows:
+        if any(k in r["Kernel_Name"] for k in _FOLLOWER) and out:
+            out[-1].append(r)
+        else:
+            out.append([r])
+    return out
 
 
 def _call_of_dispatches(n, line):
@@ -333,20 +349,20 @@ def summarize_profile(d, workload):
             raise SystemExit(f"expected one file for {pattern}, found {f}")
         return list(csv.DictReader(open(f[0])))
 
-    kt = sorted((r for r in rows(f"{w}/kt/*kernel_trace.csv") if _ours(r["Kernel_Name"])),
-                key=lambda r: int(r["Dispatch_Id"]))
+    kt = _launches(sorted((r for r in rows(f"{w}/kt/*kernel_trace.csv") if _ours(r["Kernel_Name"])),
+                          key=lambda r: int(r["Dispatch_Id"])))
     kline = _last_json(os.path.join(d, w, "kt.log"))
     kcall = _call_of_dispatches(len(kt), kline)
     labels = [c["call"] for c in kline["per_call"]]
 
     def counter(sub):
-        rs = sorted((r for r in rows(f"{w}/{sub}/*counter_collection.csv") if _ours(r["Kernel_Name"])),
-                    key=lambda r: int(r["Dispatch_Id"]))
+        rs = _launches(sorted((r for r in rows(f"{w}/{sub}/*counter_collection.csv")
+                               if _ours(r["Kernel_Name"])), key=lambda r: int(r["Dispatch_Id"])))
         line = _last_json(os.path.join(d, w, f"{sub}.log"))
         cc = _call_of_dispatches(len(rs), line)
         out = {}
-        for r, c in zip(rs, cc):
-            out.setdefault(c, []).append(float(r["Counter_Value"]) * 1024)
+        for grp, c in zip(rs, cc):
+            out.setdefault(c, []).append(sum(float(r["Counter_Value"]) for r in grp) * 1024)
         return out
 
     def copy_scale(sub, name):
@@ -358,12 +374,17 @@ def summarize_profile(d, workload):
     wscale, wkib = copy_scale("write", "WRITE_SIZE")
     fetch, write = counter("fetch"), counter("write")
     table, traffic = [], {}
+    import re
     for i, lab in enumerate(labels):
-        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000 for r, c in zip(kt, kcall) if c == i]
-        r0 = next(r for r, c in zip(kt, kcall) if c == i)
-        import re
-        m = re.search(r"(tile_kernel|gemm_kernel)<[^>]*>", r0["Kernel_Name"])
-        name = m.group(0) if m else r0["Kernel_Name"]
+        grps = [g for g, c in zip(kt, kcall) if c == i]
+        # a launch's time: its kernels' durations (a split call's reduction included)
+        durs = [sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000 for r in g) for g in grps]
+        r0 = grps[0][0]
+        names = []
+        for r in grps[0]:
+            m = re.search(r"(tile_kernel|gemm_kernel)<[^>]*>|splitk_reduce_kernel|quant_kernel", r["Kernel_Name"])
+            names.append(m.group(0) if m else r["Kernel_Name"])
+        name = " + ".join(names)
         grid = (int(r0["Grid_Size_X"]) // int(r0["Workgroup_Size_X"]), int(r0["Grid_Size_Y"]))
         fb = st.mean(fetch[i]) * fscale
         wb = st.mean(write[i]) * wscale
@@ -385,9 +406,11 @@ Commands (repository root, one MI355X, after `cd /tmp && export TMPDIR=/tmp`), t
 
 {cmds}
 
-Per call: kernel trace durations (all dispatches of that call in the traced bench run), the
-bench's own HIP-event average for the same call in that run, and HBM bytes per dispatch from
-the two counter runs, scaled by the copy calibration below.  "ratio" = measured HBM bytes /
+Per call: kernel trace durations (all launches of that call in the traced bench run; a
+split-K call's launch is its tile kernel plus the reduction kernel, durations added), the
+bench's own HIP-event average for the same call in that run (launch gaps included, and
+stretched by the tracer), and HBM bytes per launch from the two counter runs, scaled by the
+copy calibration below; grid is the first kernel's.  "ratio" = measured HBM bytes /
 algorithmic bytes (A, B, scales and D once each).
 
 | call | kernel | grid (x,y) | launches | avg us | median us | min us | bench avg us | FETCH (MB) | WRITE (MB) | algorithmic (MB) | ratio |
