@@ -272,11 +272,12 @@ def main():
 
 
 def source_sha256():
-    """sha256 over the library's kernel sources (csrc/*.hip, in name order)."""
+    """sha256 over the library's kernel sources (csrc/*.hip then csrc/*.h, in name order)."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc", "*.hip"))):
+    csrc = os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(open(f, "rb").read())
     return h.hexdigest()
 

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "e4m3.h"
 #include "fp8gemm.h"
 
 namespace {
@@ -28,28 +29,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t qrsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
-}
-
-// Magnitude code of an fp32 a = |v| (sign bit clear) in e4m3fn, round to
-// nearest even, saturating.  Finite e4m3fn values: subnormals m * 2^-9
-// (m < 8), normals (1 + m/8) * 2^(e-7) for exponent field e = 1..15 except
-// the NaN pattern 1111.111; the largest finite value is 448 (1111.110).
-__device__ __forceinline__ uint32_t e4m3_mag(uint32_t a) {
-  if (a > 0x7F800000u) return 0x7Fu;  // NaN
-  // from 464 (halfway between 448 and the next step, 480, which e4m3fn does
-  // not have) a tie to the even mantissa already gives 448; above it
-  // everything saturates to 448
-  if (a >= 0x43E80000u) return 0x7Eu;
-  if (a < 0x3C800000u) {  // below 2^-6: the subnormal grid, step 2^-9
-    // |v| * 2^9 is exact; rint rounds half to even; 8 lands on 2^-6 (0x08)
-    return (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  // normal: keep 3 of the 23 fraction bits, round the other 20 half to even;
-  // a carry out of the mantissa moves into the exponent field as it should
-  uint32_t code = ((((a >> 23) - 127u + 7u) << 3) | ((a >> 20) & 7u));
-  const uint32_t rem = a & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;
-  return code;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -85,39 +64,12 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *X, uint8_t *
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   const float s = amax == 0.f ? 1.f : amax / 448.f;
-  // x / s, correctly rounded, without a division per element: with the
-  // correctly rounded reciprocal rs of s, q0 = x rs and one exact-residual
-  // correction q0 + (x - q0 s) rs gives the correctly rounded quotient as long
-  // as the residual does not underflow.  Blocks with amax < 2^-60 are first
-  // scaled by 2^64 (x and s alike: the quotient does not change), which keeps
-  // every element that can reach a non-zero code clear of underflow.  Checked
-  // exhaustively on MI355X: the e4m3 code equals that of the IEEE quotient
-  // for every pair of positive bf16 values x <= amax.  An infinite scale (a
-  // block holding an infinity) takes the division itself.
-  const float kk = amax < 0x1p-60f ? 0x1p64f : 1.f;
-  const float sk = s * kk, rs = 1.f / sk;
-  const bool exact_div = !(s < __builtin_inff());
+  const E4m3Quotient qd(amax, s);
   uint32_t c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t w4 = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = x[4 * i + e];
-      float qv;
-      if (exact_div) {
-        qv = v / s;
-      } else {
-        const float vk = v * kk, q0 = vk * rs;
-        qv = __builtin_fmaf(__builtin_fmaf(-q0, sk, vk), rs, q0);
-      }
-      // the code's sign is x's (s > 0): NaN and -0 keep their sign
-      const uint32_t code =
-          e4m3_mag(__float_as_uint(qv) & 0x7FFFFFFFu) | ((__float_as_uint(v) >> 24) & 0x80u);
-      w4 |= code << (8 * e);
-    }
-    c[i] = w4;
-  }
+  for (int i = 0; i < 8; ++i)
+    c[i] = qd.code(x[4 * i]) | (qd.code(x[4 * i + 1]) << 8) | (qd.code(x[4 * i + 2]) << 16) |
+           (qd.code(x[4 * i + 3]) << 24);
   if (live) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(A + (size_t)m * K + kb * 128 + q * 32);
     dst[0] = u32x4{c[0], c[1], c[2], c[3]};

@@ -48,6 +48,8 @@ def _bind(lib):
     lib.fp8ref_e4m3_encode.restype = ctypes.c_uint8
     lib.fp8ref_quantize_1x128.argtypes = [vp, i32, i32, vp, vp]
     lib.fp8ref_quantize_1x128.restype = i32
+    lib.fp8ref_swiglu_quant.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, i32]
+    lib.fp8ref_swiglu_quant.restype = i32
     lib.fp8ref_points.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp,
                                   vp, vp, vp]
     for f in (lib.fp8ref_gemm, lib.fp8ref_grouped_contiguous, lib.fp8ref_grouped_masked,
@@ -187,4 +189,26 @@ def quantize_1x128(x_bf16_bits, lib=None):
     if rc:
         raise ValueError("fp8ref_quantize_1x128: bad shape")
     return codes, sa
+
+
+def swiglu_quant(kind, A, sa, B, sb, idx, codes, scales, threads=None, lib=None):
+    """Grouped GEMM with B_g = [W_gate; W_up] (2I rows), SwiGLU and 1x128
+    requantisation of y = silu(g) * u.  kind "contiguous": A [M,K],
+    sa [K/128,M], idx = m_indices [M], codes [M,I], scales [I/128,M];
+    kind "masked": A [G,M,K], sa [G,K/128,M], idx = masked_m [G],
+    codes [G,M,I], scales [G,I/128,M].  codes / scales are updated in place
+    (rows not computed keep their contents) and returned."""
+    k = {"contiguous": 1, "masked": 2}[kind]
+    A, B = _c(A, np.uint8), _c(B, np.uint8)
+    sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+    idx = _c(idx, np.int32)
+    G, N2, K = B.shape
+    I = N2 // 2
+    M = A.shape[0] if kind == "contiguous" else A.shape[1]
+    assert codes.flags.c_contiguous and scales.flags.c_contiguous
+    rc = (lib or load()).fp8ref_swiglu_quant(k, _p(A), _p(sa), _p(B), _p(sb), M, I, K, G, _p(idx),
+                                              _p(codes), _p(scales), _threads(threads))
+    if rc:
+        raise ValueError("fp8ref_swiglu_quant: bad arguments")
+    return codes, scales
 

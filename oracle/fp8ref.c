@@ -137,7 +137,12 @@ typedef struct {
   int M, N, K, G;
   const int32_t *m_indices, *masked_m;
   long row_begin, row_end; /* rows of the flattened output: dense/contig m, masked g*M+m */
+  uint8_t *act;            /* SwiGLU form (N = 2I): codes [rows][I] and scales ... */
+  float *act_scale;        /* ... [G or 1][I/128][M]; D and D64 unused */
 } job_t;
+
+static void swiglu_row(const job_t *j, const uint8_t *A, const float *sa, const uint8_t *B,
+                       const float *sb, long row, long m, long g);
 
 static void do_row(const job_t *j, long row) {
   int Kb = j->K / 128, Nb = (j->N + 127) / 128;
@@ -164,6 +169,10 @@ static void do_row(const job_t *j, long row) {
     sa += g * (long)Kb * M;
     B += g * N * K;
     sb += g * (long)Nb * Kb;
+  }
+  if (j->act) {
+    swiglu_row(j, A, sa, B, sb, row, m, j->kind == MASKED ? row / M : 0);
+    return;
   }
   for (long n = 0; n < N; ++n) {
 #if MUTANT == 6 /* planted mistake: B read transposed-in-blocks (column n uses row n^1) */
@@ -351,3 +360,66 @@ int fp8ref_quantize_1x128(const uint16_t *x, int M, int K, uint8_t *codes, float
     }
   return 0;
 }
+
+/* ---- grouped GEMM with a fused SwiGLU and 1x128 requantisation ----------
+ * The step after the grouped GEMM in an MoE expert (kakushin, "Hva gjør
+ * DeepGEMM?": the fused MoE flow includes the activation).  B_g holds
+ * [W_gate; W_up]: rows 0..I-1 gate, rows I..2I-1 up (N = 2I, I % 128 == 0).
+ * For a computed row m (the GEMM's rules: contiguous m_indices[m] in [0,G),
+ * masked m < clamp(masked_m[g], 0, M)) and n < I:
+ *   g = GEMM(m, n), u = GEMM(m, I + n)   the GEMM oracle's exact values,
+ *   y = silu(g) * u = g u / (1 + e^-g)   in fp64, rounded once to fp32;
+ * each 128-wide block of y is then quantised like fp8ref_quantize_1x128
+ * (s = amax|y| / 448 in fp32, codes of y / s, the sign of y).  Codes are
+ * [M][I] (masked [G][M][I]); scales [I/128][M] (masked [G][I/128][M]); rows
+ * not computed keep their previous contents. */
+static void swiglu_row(const job_t *j, const uint8_t *A, const float *sa, const uint8_t *B,
+                       const float *sb, long row, long m, long g) {
+  const long M = j->M, K = j->K, I = j->N / 2;
+  const int Kb = j->K / 128;
+  float y[128];
+  for (long b = 0; b < I / 128; ++b) {
+    float amax = 0.0f;
+    for (long c = 0; c < 128; ++c) {
+      const long n = b * 128 + c;
+      const double gv = element(A + m * K, sa + m, M, B + n * K, sb + (n / 128) * Kb, Kb);
+      const double uv = element(A + m * K, sa + m, M, B + (I + n) * K, sb + ((I + n) / 128) * Kb, Kb);
+#if MUTANT == 9 /* planted mistake: gate and up swapped */
+      y[c] = (float)(uv / (1.0 + exp(-uv)) * gv);
+#else
+      y[c] = (float)(gv / (1.0 + exp(-gv)) * uv);
+#endif
+      const float a = fabsf(y[c]);
+      if (a > amax) amax = a;
+    }
+    const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+    j->act_scale[(g * (I / 128) + b) * M + m] = s;
+    for (long c = 0; c < 128; ++c)
+      j->act[row * I + b * 128 + c] =
+          (uint8_t)(fp8ref_e4m3_encode(fabsf(y[c] / s)) | (signbit(y[c]) ? 0x80 : 0x00));
+  }
+}
+
+int fp8ref_swiglu_quant(int kind, const uint8_t *A, const float *sa, const uint8_t *B,
+                        const float *sb, int M, int I, int K, int G, const int32_t *idx,
+                        uint8_t *codes, float *scales, int threads) {
+  if (bad_dims(M, 2 * I, K) || I % 128 != 0 || G < 1 || (kind != CONTIG && kind != MASKED))
+    return 1;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.kind = kind;
+  j.A = A;
+  j.B = B;
+  j.sa = sa;
+  j.sb = sb;
+  j.M = M;
+  j.N = 2 * I;
+  j.K = K;
+  j.G = G;
+  j.m_indices = kind == CONTIG ? idx : NULL;
+  j.masked_m = kind == MASKED ? idx : NULL;
+  j.act = codes;
+  j.act_scale = scales;
+  return run(j, kind == MASKED ? (long)G * M : (long)M, threads);
+}
+

@@ -482,6 +482,69 @@ def test_quantize_1x128_error_bound():
     assert (np.abs(deq - x) <= bound * (1 + 1e-6)).all()
 
 
+# ------------------------------- grouped GEMM + SwiGLU + requantisation ----
+
+
+def independent_swiglu_quant(A, sa, Bg, sbg):
+    """dequantise, fp64 matmul, y = g u / (1 + e^-g) rounded to fp32, then the
+    1x128 quantisation through numpy and PyTorch's float8 cast"""
+    M, K = A.shape
+    I = Bg.shape[0] // 2
+    Ad = TV[A] * np.repeat(sa.T.astype(np.float64), 128, axis=1)
+    Bd = TV[Bg] * np.repeat(np.repeat(sbg.astype(np.float64), 128, axis=1), 128, axis=0)[:2 * I]
+    h = Ad @ Bd.T
+    g, u = h[:, :I], h[:, I:]
+    with np.errstate(over="ignore"):  # e^-g overflows for very negative g: silu -> -0
+        y = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    codes = np.empty((M, I), np.uint8)
+    scales = np.empty((I // 128, M), np.float32)
+    for b in range(I // 128):
+        blk = y[:, b * 128:(b + 1) * 128]
+        amax = np.abs(blk).max(axis=1)
+        s = np.where(amax == 0, np.float32(1), (amax / np.float32(448)).astype(np.float32)).astype(np.float32)
+        scales[b] = s
+        q = np.abs((blk / s[:, None]).astype(np.float32))
+        codes[:, b * 128:(b + 1) * 128] = torch_e4m3_bits(q) | np.where(np.signbit(blk), 0x80, 0).astype(np.uint8)
+    return codes, scales
+
+
+def test_swiglu_quant_matches_independent_chain():
+    rng = np.random.default_rng(41)
+    G, M, I, K = 2, 6, 256, 384
+    A = rand_codes(rng, (M, K))
+    sa = rng.uniform(0.01, 0.1, (K // 128, M)).astype(np.float32)
+    B = rand_codes(rng, (G, 2 * I, K))
+    sb = rng.uniform(0.01, 0.1, (G, 2 * I // 128, K // 128)).astype(np.float32)
+    idx = np.array([0, 1, -1, 1, 0, 0], np.int32)
+    codes = np.full((M, I), 0xAB, np.uint8)
+    scales = np.full((I // 128, M), -7.0, np.float32)
+    oracle.swiglu_quant("contiguous", A, sa, B, sb, idx, codes, scales)
+    for m in range(M):
+        if idx[m] < 0:  # padding row: untouched
+            assert (codes[m] == 0xAB).all() and (scales[:, m] == -7.0).all()
+            continue
+        c, sc = independent_swiglu_quant(A[m:m + 1], sa[:, m:m + 1], B[idx[m]], sb[idx[m]])
+        assert (codes[m] == c[0]).all() and (scales[:, m] == sc[:, 0]).all()
+
+
+def test_swiglu_quant_masked_rows_and_zero_gate():
+    rng = np.random.default_rng(42)
+    G, M, I, K = 2, 5, 128, 256
+    A = rand_codes(rng, (G, M, K))
+    sa = rng.uniform(0.01, 0.1, (G, K // 128, M)).astype(np.float32)
+    B = rand_codes(rng, (G, 2 * I, K))
+    B[1, :I] = 0  # expert 1's gate rows are zero: silu(0) = 0 everywhere
+    sb = rng.uniform(0.01, 0.1, (G, 2, K // 128)).astype(np.float32)
+    mm = np.array([3, 9], np.int32)  # 9 is clamped to M
+    codes = np.full((G, M, I), 0xAB, np.uint8)
+    scales = np.full((G, I // 128, M), -7.0, np.float32)
+    oracle.swiglu_quant("masked", A, sa, B, sb, mm, codes, scales)
+    assert (codes[0, 3:] == 0xAB).all() and (scales[0, :, 3:] == -7.0).all()
+    assert (codes[1] & 0x7F == 0).all() and (scales[1] == 1.0).all()  # y == 0: scale 1, zero codes
+    c, sc = independent_swiglu_quant(A[0, :3], sa[0, :, :3], B[0], sb[0])
+    assert (codes[0, :3] == c).all() and (scales[0, :, :3] == sc).all()
+
+
 # ------------------------------------------------------ planted mistakes ----
 
 MUTANTS = {
@@ -493,6 +556,7 @@ MUTANTS = {
     6: "pairs output column n with weight row n^1",
     7: "rounds e4m3 ties towards the larger code",
     8: "quantises with scale amax / 447",
+    9: "swaps the gate and up halves of the SwiGLU",
 }
 
 
@@ -529,6 +593,17 @@ def _pins_pass(lib):
     codes, sa = oracle.quantize_1x128(xb, lib=lib)
     if sa[0, 0] != 2.0 or codes[0, 5] != 0x7E:
         failed.append("quantise_scale")
+    # SwiGLU: one row, one block; against the independent chain
+    A3 = rand_codes(rng, (1, 128))
+    B3 = rand_codes(rng, (1, 256, 128))
+    sa3 = np.full((1, 1), 0.05, np.float32)
+    sb3 = np.full((1, 2, 1), 0.05, np.float32)
+    c3 = np.zeros((1, 128), np.uint8)
+    s3 = np.zeros((1, 1), np.float32)
+    oracle.swiglu_quant("contiguous", A3, sa3, B3, sb3, np.zeros(1, np.int32), c3, s3, lib=lib)
+    ci, si = independent_swiglu_quant(A3, sa3, B3[0], sb3[0])
+    if not ((c3 == ci).all() and (s3 == si).all()):
+        failed.append("swiglu")
     return failed
 
 
