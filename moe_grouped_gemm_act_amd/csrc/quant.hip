@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *X, uint8_t *
   uint32_t c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    c[i] = qd.code(x[4 * i]) | (qd.code(x[4 * i + 1]) << 8) | (qd.code(x[4 * i + 2]) << 16) |
-           (qd.code(x[4 * i + 3]) << 24);
+    c[i] = e4m3_pack4(qd.quotient(x[4 * i]), qd.quotient(x[4 * i + 1]), qd.quotient(x[4 * i + 2]),
+                      qd.quotient(x[4 * i + 3]), x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
   if (live) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(A + (size_t)m * K + kb * 128 + q * 32);
     dst[0] = u32x4{c[0], c[1], c[2], c[3]};
