@@ -60,11 +60,17 @@ class Call:
             M, K = self.d["M"], self.d["K"]
             return {"X": X, "A": torch.empty((M, K), dtype=torch.uint8, device=dev),
                     "sa": torch.empty((K // 128, M), dtype=torch.float32, device=dev)}
-        keys = ["A", "sa", "B", "sb"] + (["m_indices"] if self.kind == "contiguous" else []) \
-            + (["masked_m"] if self.kind == "masked" else [])
+        base = self.kind.replace("_swiglu", "")
+        keys = ["A", "sa", "B", "sb"] + (["m_indices"] if base == "contiguous" else []) \
+            + (["masked_m"] if base == "masked" else [])
         t = {k: torch.from_numpy(self.d[k]).to(dev) for k in keys}
-        shape = (self.d["G"], self.d["M"], self.d["N"]) if self.kind == "masked" else (self.d["M"], self.d["N"])
-        t["D"] = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        lead = (self.d["G"],) if base == "masked" else ()
+        M, N = self.d["M"], self.d["N"]
+        if self.kind.endswith("_swiglu"):
+            t["Y"] = torch.empty((*lead, M, N // 2), dtype=torch.uint8, device=dev)
+            t["sy"] = torch.empty((*lead, N // 256, M), dtype=torch.float32, device=dev)
+        else:
+            t["D"] = torch.empty((*lead, M, N), dtype=torch.bfloat16, device=dev)
         return t
 
     def launch(self, fg, t):
@@ -74,6 +80,12 @@ class Call:
             fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
         elif self.kind == "contiguous":
             fg.grouped_contiguous(t["A"], t["sa"], t["B"], t["sb"], t["m_indices"], t["D"])
+        elif self.kind == "contiguous_swiglu":
+            fg.grouped_contiguous_swiglu_fp8(t["A"], t["sa"], t["B"], t["sb"], t["m_indices"],
+                                             t["Y"], t["sy"])
+        elif self.kind == "masked_swiglu":
+            fg.grouped_masked_swiglu_fp8(t["A"], t["sa"], t["B"], t["sb"], t["masked_m"],
+                                         self.d["expected_m"], t["Y"], t["sy"])
         else:
             fg.grouped_masked(t["A"], t["sa"], t["B"], t["sb"], t["masked_m"], self.d["expected_m"], t["D"])
 
@@ -103,6 +115,22 @@ def workload_calls(name):
             xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
             d = {"X": xb, "M": M, "K": K}
             calls.append(Call("quant", d, f"quantize {M}x{K}", 0.0, 3 * M * K + 4 * M * (K // 128)))
+    elif name == "swiglu":
+        # the experts' gate/up projection (N = 2I = 4096, K = 7168) with the
+        # SwiGLU and 1x128 requantisation fused: codes [rows, I] and scales
+        # [I/128, rows] are written instead of a bf16 D
+        for i, (G, rows, N, K, uniform) in enumerate(W.CONTIG_CASES):
+            d = W.contiguous(4000 + i, G, rows, N, K, uniform)
+            counts = np.bincount(d["m_indices"][d["m_indices"] >= 0], minlength=G)
+            flop, by = grouped_cost(counts.tolist(), N, K)
+            by += int(counts.sum()) * (N // 2 + 4 * (N // 256) - 2 * N) + 4 * rows
+            calls.append(Call("contiguous_swiglu", d, f"contiguous+swiglu G={G} {rows}x{N}x{K}", flop, by))
+        G, M, N, K = W.MASKED_CASES[0]
+        d = W.masked(5000, G, M, N, K)
+        live = np.clip(d["masked_m"], 0, M)
+        flop, by = grouped_cost(live.tolist(), N, K)
+        by += int(live.sum()) * (N // 2 + 4 * (N // 256) - 2 * N) + 4 * G
+        calls.append(Call("masked_swiglu", d, f"masked+swiglu G={G} {M}x{N}x{K}", flop, by))
     elif name == "masked":
         for i, (G, M, N, K) in enumerate(W.MASKED_CASES):
             d = W.masked(5000 + i, G, M, N, K)
@@ -119,6 +147,7 @@ WORKLOAD_TEXT = {
     "small": "dense FP8 GEMM 128x256x512",
     "contiguous": "MoE grouped FP8 GEMM, M-axis contiguous: G=4 x 8192 rows and G=8 uneven (32768 padded rows), N=4096, K=7168",
     "masked": "MoE grouped FP8 GEMM, masked: G=16, 256 rows/expert, masked_m ~ U[0,256], (N,K) in {(4096,7168),(7168,2048)}",
+    "swiglu": "MoE gate/up projection with SwiGLU and 1x128 FP8 requantisation fused: contiguous G=4 x 8192 rows and G=8 uneven (32768 padded rows), masked G=16 x 256 rows; N=2I=4096, K=7168",
     "quant": "1x128 FP8 quantisation of bf16 activations, M=4096 x K in {16384,7168,1536,18432} (the prefill A operands), 1% rows x50",
 }
 MEMORY_BOUND = {"decode", "small", "masked", "quant"}
@@ -467,9 +496,9 @@ def cpu_baseline(calls, budget_s, memory_bound):
                     break
                 continue
             A, sa, B, sb = d["A"], d["sa"], d["B"], d["sb"]
-            if c.kind == "masked":
-                A, sa, B, sb = A[0], sa[0], B[0], sb[0]
-            elif c.kind == "contiguous":
+            if c.kind.startswith("masked"):
+                A, sa = A[0], sa[0]
+            if c.kind != "dense":
                 B, sb = B[0], sb[0]
             M, K = A.shape
             N = B.shape[0]
@@ -477,10 +506,19 @@ def cpu_baseline(calls, budget_s, memory_bound):
             # assumed 1e9 multiply-adds per second per thread
             left = max(0.2, budget_s - (time.perf_counter() - t0))
             rows = max(1, min(M, int(left * 1e9 * threads / (N * K))))
-            oracle.gemm(A[:rows], np.ascontiguousarray(sa[:, :rows]), B, sb, threads=threads)
+            sa_r = np.ascontiguousarray(sa[:, :rows])
+            if c.kind.endswith("_swiglu"):  # one expert's rows through the fused oracle
+                I = N // 2
+                oracle.swiglu_quant("contiguous", A[:rows], sa_r, B[None], sb[None],
+                                    np.zeros(rows, np.int32), np.empty((rows, I), np.uint8),
+                                    np.empty((I // 128, rows), np.float32), threads=threads)
+                by += rows * K + 4 * rows * (K // 128) + N * K + 4 * (N // 128) * (K // 128) \
+                    + rows * I + 4 * rows * (I // 128)
+            else:
+                oracle.gemm(A[:rows], sa_r, B, sb, threads=threads)
+                by += dense_bytes(rows, N, K)  # algorithmic bytes of the computed slice
             if passes == 0:
                 done.append(f"{rows}x{N}x{K}")
-            by += dense_bytes(rows, N, K)  # algorithmic bytes of the computed slice
             fl += 2.0 * rows * N * K
             if time.perf_counter() - t0 > budget_s:
                 break

@@ -129,6 +129,43 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
  */
 int quantize_fp8_1x128(const void *X, void *A, float *sa, int M, int K, void *stream);
 
+/*
+ * Grouped GEMM with the expert's activation fused into its epilogue: the
+ * linear layer and the activation that the pages' fused MoE flow chains
+ * (kakushin.no, "Hva gjør DeepGEMM?", the Mega MoE item).  The pages name no
+ * activation; this is the SwiGLU reading, followed by the 1x128 FP8
+ * requantisation the next expert GEMM reads, so y never goes to memory in
+ * a wider type.
+ *   Each expert's weights B_g [2I,K] stack the gate projection (rows 0..I-1)
+ *   over the up projection (rows I..2I-1), with sb_g [2I/128][K/128].  With
+ *   h = the fp32 block-scaled sum of the calls above, taken before any bf16
+ *   rounding,
+ *     y[m,n] = silu(h[m,n]) * h[m,I+n],   silu(x) = x / (1 + e^-x),  n < I,
+ *   is quantised per row and 128-wide block of n as quantize_fp8_1x128
+ *   quantises x (the same scale and code rules, applied to the fp32 y):
+ *   codes Y [.., I] and scales sy [I/128][M] (M contiguous).  y is formed
+ *   in fp32 with the hardware exponential and reciprocal, from h as the
+ *   MFMA block sums give it, so it is not the exact y: a code may be one
+ *   step off where the exact y / s lies near a rounding midpoint (about 0.1%
+ *   of codes on random data), and a scale a few fp32 ulps off.
+ * Rows are selected as in the grouped calls above; rows not computed keep
+ * their previous codes and scales.  No bf16 output is written.
+ * Constraints beyond the grouped calls: I % 128 == 0 and K <= 20480
+ * (FP8GEMM_UNSUPPORTED_SHAPE otherwise); sy 4-byte aligned; Y 16-byte
+ * aligned.  Allocates nothing.
+ */
+/* Contiguous layout: A [M,K], sa [K/128][M], B [G][2I,K],
+ * sb [G][2I/128][K/128], m_indices [M]; Y [M,I], sy [I/128][M]. */
+int grouped_contiguous_swiglu_fp8(const void *A, const float *sa, const void *B, const float *sb,
+                                  void *Y, float *sy, int M, int I, int K, int G, void *stream,
+                                  const int32_t *m_indices);
+
+/* Masked layout: A [G][M,K], sa [G][K/128][M], B [G][2I,K],
+ * sb [G][2I/128][K/128], masked_m [G]; Y [G][M,I], sy [G][I/128][M]. */
+int grouped_masked_swiglu_fp8(const void *A, const float *sa, const void *B, const float *sb,
+                              void *Y, float *sy, int M, int I, int K, int G, void *stream,
+                              const int32_t *masked_m, int expected_m);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8gemm_status_string(int status);
 

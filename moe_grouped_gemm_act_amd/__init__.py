@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8gemm.h")
 
 __all__ = ["gemm_fp8_1x128_128x128_bf16", "grouped_contiguous", "grouped_masked",
-           "quantize_fp8_1x128", "fp8gemm_status_string", "Fp8GemmError", "load_library",
+           "quantize_fp8_1x128", "grouped_contiguous_swiglu_fp8", "grouped_masked_swiglu_fp8",
+           "fp8gemm_status_string", "Fp8GemmError", "load_library",
            "LIB_PATH"]
 
 
@@ -49,8 +50,13 @@ def load_library():
         lib.grouped_contiguous.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
         lib.grouped_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32]
         lib.quantize_fp8_1x128.argtypes = [vp, vp, vp, i32, i32, vp]
+        lib.grouped_contiguous_swiglu_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                      vp, vp]
+        lib.grouped_masked_swiglu_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                  vp, i32]
         for f in (lib.gemm_fp8_1x128_128x128_bf16, lib.grouped_contiguous, lib.grouped_masked,
-                  lib.quantize_fp8_1x128):
+                  lib.quantize_fp8_1x128, lib.grouped_contiguous_swiglu_fp8,
+                  lib.grouped_masked_swiglu_fp8):
             f.restype = i32
         lib.fp8gemm_status_string.argtypes = [i32]
         lib.fp8gemm_status_string.restype = ctypes.c_char_p
@@ -188,3 +194,62 @@ def quantize_fp8_1x128(X, A=None, sa=None, stream=None):
     dev = _dev(X, A, sa)
     _check(load_library().quantize_fp8_1x128(_p(X), _p(A), _p(sa), M, K, _stream(stream, dev)))
     return A, sa
+
+
+def _swiglu_outputs(Y, sy, lead, M, I, dev):
+    if Y is None:
+        Y = torch.empty((*lead, M, I), dtype=torch.uint8, device=dev)
+    if sy is None:
+        sy = torch.empty((*lead, I // 128, M), dtype=torch.float32, device=dev)
+    Y = _codes(Y, "Y")
+    _shape(Y, (*lead, M, I), "Y")
+    _shape(sy, (*lead, I // 128, M), "sy")
+    if sy.dtype != torch.float32:
+        raise TypeError("sy must be float32")
+    return Y, sy
+
+
+def grouped_contiguous_swiglu_fp8(A, sa, B, sb, m_indices, Y=None, sy=None, stream=None):
+    """Contiguous grouping with SwiGLU and 1x128 requantisation fused:
+    A [M,K], sa [K/128,M], B [G,2I,K] (gate rows over up rows),
+    sb [G,2I/128,K/128], m_indices [M] int32.  Returns (Y [M,I] e4m3fn codes
+    as uint8, sy [I/128,M] float32); rows whose index is outside [0,G) are
+    not written."""
+    A, B = _codes(A, "A"), _codes(B, "B")
+    M, K = A.shape
+    G, N2 = B.shape[0], B.shape[1]
+    I = N2 // 2
+    _shape(B, (G, 2 * I, K), "B")
+    _shape(sa, (K // 128, M), "sa")
+    _shape(sb, (G, (2 * I + 127) // 128, K // 128), "sb")
+    _shape(m_indices, (M,), "m_indices")
+    if m_indices.dtype != torch.int32:
+        raise TypeError("m_indices must be int32")
+    Y, sy = _swiglu_outputs(Y, sy, (), M, I, A.device)
+    dev = _dev(A, sa, B, sb, m_indices, Y, sy)
+    _check(load_library().grouped_contiguous_swiglu_fp8(
+        _p(A), _p(sa), _p(B), _p(sb), _p(Y), _p(sy), M, I, K, G, _stream(stream, dev),
+        _p(m_indices)))
+    return Y, sy
+
+
+def grouped_masked_swiglu_fp8(A, sa, B, sb, masked_m, expected_m, Y=None, sy=None, stream=None):
+    """Masked grouping with SwiGLU and 1x128 requantisation fused:
+    A [G,M,K], sa [G,K/128,M], B [G,2I,K], sb [G,2I/128,K/128], masked_m [G]
+    int32.  Returns (Y [G,M,I] codes, sy [G,I/128,M]); only rows
+    m < masked_m[g] are written."""
+    A, B = _codes(A, "A"), _codes(B, "B")
+    G, M, K = A.shape
+    I = B.shape[1] // 2
+    _shape(B, (G, 2 * I, K), "B")
+    _shape(sa, (G, K // 128, M), "sa")
+    _shape(sb, (G, (2 * I + 127) // 128, K // 128), "sb")
+    _shape(masked_m, (G,), "masked_m")
+    if masked_m.dtype != torch.int32:
+        raise TypeError("masked_m must be int32")
+    Y, sy = _swiglu_outputs(Y, sy, (G,), M, I, A.device)
+    dev = _dev(A, sa, B, sb, masked_m, Y, sy)
+    _check(load_library().grouped_masked_swiglu_fp8(
+        _p(A), _p(sa), _p(B), _p(sb), _p(Y), _p(sy), M, I, K, G, _stream(stream, dev),
+        _p(masked_m), int(expected_m)))
+    return Y, sy

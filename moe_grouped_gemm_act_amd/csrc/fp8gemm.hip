@@ -43,6 +43,7 @@
 #include <map>
 #include <mutex>
 
+#include "e4m3.h"
 #include "fp8gemm.h"
 
 namespace {
@@ -68,6 +69,8 @@ struct Args {
   int tiles_m, tiles_n;
   int splits, kb_per_split;  // K split over workgroups (tile kernel, dense only); 1 and K/128 otherwise
   float *ws;                 // split-K partial planes [splits][M][N] (splits > 1)
+  uint8_t *act;              // fused SwiGLU: e4m3 codes of y [M][N/2] (masked [G][M][N/2]) ...
+  float *act_scale;          // ... and their 1x128 scales [N/256][M] ([G][N/256][M])
 };
 
 // XOR key of an LDS row: 16-byte chunk c of row r sits at position
@@ -305,7 +308,17 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F
 // and ends; splitk_reduce_kernel, launched next on the same stream, adds the
 // planes in split order and rounds to bf16, spread over the whole chip.  The
 // result is deterministic, and nothing waits on another workgroup.
-template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, int LAYOUT>
+// The lane id computed anew where it is called (the compiler cannot merge it
+// with an earlier copy), so a lane-derived value needed after the K loop
+// need not be kept live through it, where the compute waves use every
+// register.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, bool ACT, int LAYOUT>
 __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   constexpr int ROWS = BM + BN;
@@ -321,8 +334,12 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 64 == 0 &&
                     128 % (TN * 16) == 0, "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
+  // ACT (fused SwiGLU): the tile's weight rows are 128 gate rows (waves
+  // wn < WGN/2) and the 128 matching up rows; its output is 128 columns of y
+  static_assert(!ACT || (BN == 256 && WGN == 4 && TN == 4 && BM <= 128), "SwiGLU tile shape");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ float s_sb[BN > 128 ? 2 : 1][MAXKB];
+  __shared__ float s_rmax[ACT ? 2 : 1][ACT ? BM : 1];  // ACT: row maxima of y per gate wave column
   __shared__ int s_group;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -355,6 +372,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   const uint8_t *A = a.A, *B = a.B;
   const float *sa = a.sa, *sb = a.sb;
   uint16_t *D = a.D;
+  uint8_t *act = a.act;
+  float *act_scale = a.act_scale;
   int mvalid = M, g = 0;
   if (LAYOUT == MASKED) {
     g = blockIdx.y;
@@ -364,6 +383,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     A += (size_t)g * M * K;
     sa += (size_t)g * Kb * M;
     D += (size_t)g * M * N;
+    act += (size_t)g * M * (N / 2);
+    act_scale += (size_t)g * (N / 256) * M;
   }
   if (LAYOUT == CONTIG) {
     if (tid == 0) s_group = -1;
@@ -383,6 +404,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   if (wave >= NCW) {
     // ---------------- loader waves ----------------
     const int L = wave - NCW;
+    const int lane = ACT ? fresh_lane_id() : tid & 63;
     constexpr int QA = BM / 8 / NLD;  // loads q < QA are activation row groups, the rest weights
     static_assert((BM / 8) % NLD == 0, "row groups split evenly between A and B");
     const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint32_t)M * K);
@@ -397,10 +419,14 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     for (int q = 0; q < DMA; ++q) {
       const int r = (L + NLD * q) * 8 + (lane >> 3);
       const int col = (lane & 7) ^ row_key(r);
-      if (q < QA)
+      if (q < QA) {
         off[q] = m0 + r < mvalid ? (uint32_t)(m0 + r) * K + col * 16 : OOB;
-      else
-        off[q] = n0 + r - BM < N ? (uint32_t)(n0 + r - BM) * K + col * 16 : OOB;
+      } else {
+        const int rw = r - BM;  // weight row of the tile
+        // ACT: gate rows 128 tn + rw, then up rows N/2 + 128 tn + (rw - 128)
+        const int grow = ACT ? (rw < 128 ? tn * 128 + rw : N / 2 + tn * 128 + rw - 128) : n0 + rw;
+        off[q] = grow < N ? (uint32_t)grow * K + col * 16 : OOB;
+      }
     }
     uint32_t soff[SPL];  // byte offsets of scale floats 64 j + lane of the tile's rows
     int sdst[SPL];
@@ -439,11 +465,18 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     }
 #undef TK_G
     __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
+    if (ACT) {                      // the three barriers of the SwiGLU epilogue
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+    }
     return;
   }
 
   // ---------------- compute waves ----------------
-  const int wn = wave % WGN, wm = wave / WGN;
+  // ACT: waves 0-3 take the gate columns (wn < 2), one per SIMD, so the
+  // epilogue's arithmetic, which only they do, is spread over the four SIMDs
+  const int wn = ACT ? wave >> 1 : wave % WGN, wm = ACT ? wave & 1 : wave / WGN;
   const int hsb = (wn * TN * 16) / 128;  // which weight-scale block this wave's rows use
   v4f acc[TN][TM];
 #pragma unroll
@@ -454,7 +487,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   // first K-block barrier publishes them
   for (int i = tid; i < (BN > 128 ? 2 : 1) * nk; i += CT) {
     const int h = i / nk, t = i % nk;
-    s_sb[h][t] = sb[(size_t)min(n0 / 128 + h, Nb - 1) * Kb + kb0 + t];
+    const int blk = ACT ? (h == 0 ? tn : N / 256 + tn) : min(n0 / 128 + h, Nb - 1);
+    s_sb[h][t] = sb[(size_t)blk * Kb + kb0 + t];
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -479,7 +513,12 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();  // block t is in slot u
       asm volatile("" ::: "memory");
-      const uint8_t *sl = lds[u];
+      // ACT: the slot's offset goes through an empty asm, so the compiler
+      // adds it at each read instead of keeping every slot's fragment
+      // addresses in registers through the loop
+      int so = u * SLOT;
+      if (ACT) asm volatile("" : "+s"(so));
+      const uint8_t *sl = &lds[0][0] + so;
       const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
       const float sbv = s_sb[hsb][t];
       v8i bfr[TN], afr[2];
@@ -523,6 +562,74 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
+
+  if constexpr (ACT) {
+    // Fused SwiGLU and 1x128 requantisation of y = silu(g) u.  Gate values sit
+    // in waves wn < 2 and the matching up values in waves wn + 2 (same lanes);
+    // the up values cross over through the LDS ring, free once every wave is
+    // past the K loop.  A row's 128 outputs are held by the two gate waves of
+    // its activation group: their maxima meet in LDS, and both then encode
+    // their half with the block scale s = amax|y| / 448.
+    constexpr int UPS = 132;  // floats per exchange row (16-byte aligned rows)
+    static_assert(BM * UPS * 4 <= STAGES * SLOT, "up-value exchange fits the ring");
+    float *up = reinterpret_cast<float *>(&lds[0][0]);
+    const int I = N / 2;
+    const int lid = fresh_lane_id();
+    const int fr = lid & 15, fg = lid >> 4;
+    __syncthreads();  // (1) the loaders have drained: the ring may be reused
+    if (wn >= 2) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          *reinterpret_cast<v4f *>(up + ((wm * TM + j) * 16 + fr) * UPS + (wn - 2) * 64 + i * 16 +
+                                   4 * fg) = acc[i][j];
+    }
+    __syncthreads();  // (2) up values in LDS
+    if (wn < 2) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const v4f u4 = *reinterpret_cast<const v4f *>(
+              up + ((wm * TM + j) * 16 + fr) * UPS + wn * 64 + i * 16 + 4 * fg);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = acc[i][j][r];
+            // silu(g) = g / (1 + e^-g): hardware exponential and reciprocal
+            acc[i][j][r] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * u4[r];
+            mx = fmaxf(mx, fabsf(acc[i][j][r]));  // NaN is skipped, as in the quantiser
+          }
+        }
+        // the row's other 48 values of this wave sit in lanes fr + 16, + 32, + 48
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (fg == 0) s_rmax[wn][(wm * TM + j) * 16 + fr] = mx;
+      }
+    }
+    __syncthreads();  // (3) row maxima of both gate waves
+    if (wn < 2) {
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int ml = (wm * TM + j) * 16 + fr, m = m0 + ml;
+        const float amax = fmaxf(s_rmax[0][ml], s_rmax[1][ml]);
+        const float sc = amax == 0.f ? 1.f : amax / 448.f;
+        const E4m3Quotient qd(amax, sc);
+        bool ok = m < mvalid;
+        if (LAYOUT == CONTIG) ok = m < M && a.idx[m] == g;
+        if (!ok) continue;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+          *reinterpret_cast<uint32_t *>(act + (size_t)m * I + tn * 128 + wn * 64 + i * 16 + 4 * fg) =
+              e4m3_pack4(qd.quotient(acc[i][j][0]), qd.quotient(acc[i][j][1]),
+                         qd.quotient(acc[i][j][2]), qd.quotient(acc[i][j][3]), acc[i][j][0],
+                         acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        if (wn == 0 && fg == 0) act_scale[(size_t)tn * M + m] = sc;
+      }
+    }
+    return;
+  }
 
   if (S > 1) {
     // this split's fp32 partial goes to its own [M][N] plane of the
@@ -648,7 +755,8 @@ const Workspace *workspace(hipStream_t s) {
   return &(g_ws[{dev, s}] = w);
 }
 
-template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool KSPLIT = false>
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool KSPLIT = false,
+          bool ACT = false>
 int launch_tile(Args a, int groups, hipStream_t stream) {
   a.tiles_m = cdiv(a.M, WGM * TM * 16);
   a.tiles_n = cdiv(a.N, WGN * TN * 16);
@@ -658,7 +766,7 @@ int launch_tile(Args a, int groups, hipStream_t stream) {
   }
   void *kargs[] = {&a};
   hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, KSPLIT, LAYOUT>),
+      reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, KSPLIT, ACT, LAYOUT>),
       dim3(a.tiles_m * a.tiles_n * a.splits, groups), dim3((WGN * WGM + NLD) * 64), kargs, 0,
       stream);
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
@@ -822,6 +930,46 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   // 64-row activation tiles when the hint says counts are small
   if (expected_m <= 64) return launch_tile<1, 4, 8, 1, 4, 4, MASKED>(a, G, s);
   return launch_tile<1, 4, 8, 2, 4, 4, MASKED>(a, G, s);
+}
+
+// Grouped GEMM with B_g = [W_gate; W_up] (N = 2I rows) and the SwiGLU and
+// 1x128 requantisation fused into the epilogue; shared checks.
+static int check_swiglu(const void *A, const float *sa, const void *B, const float *sb,
+                        const void *Y, const float *sy, int M, int I, int K, int G,
+                        const int32_t *idx, long long a_elems, long long y_elems) {
+  if (G < 1 || I < 0) return FP8GEMM_INVALID_ARG;
+  const int st = check_common(A, sa, B, sb, Y, M, 2 * I, K, a_elems, (long long)G * 2 * I * K,
+                              y_elems);
+  if (st != FP8GEMM_OK) return st;
+  if (!sy || !idx) return FP8GEMM_INVALID_ARG;
+  if (!aligned(sy, 4) || !aligned(idx, 4)) return FP8GEMM_MISALIGNED;
+  if (I % 128 != 0 || K > 20480) return FP8GEMM_UNSUPPORTED_SHAPE;
+  return FP8GEMM_OK;
+}
+
+int grouped_contiguous_swiglu_fp8(const void *A, const float *sa, const void *B, const float *sb,
+                                  void *Y, float *sy, int M, int I, int K, int G, void *stream,
+                                  const int32_t *m_indices) {
+  const int st = check_swiglu(A, sa, B, sb, Y, sy, M, I, K, G, m_indices, (long long)M * K,
+                              (long long)M * I);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
+  Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb, nullptr, M,
+         2 * I, K, G, m_indices, 0, 0, 1, K / BK, nullptr, static_cast<uint8_t *>(Y), sy};
+  return launch_tile<4, 2, 4, 4, 3, 4, CONTIG, false, true>(a, 1, static_cast<hipStream_t>(stream));
+}
+
+int grouped_masked_swiglu_fp8(const void *A, const float *sa, const void *B, const float *sb,
+                              void *Y, float *sy, int M, int I, int K, int G, void *stream,
+                              const int32_t *masked_m, int expected_m) {
+  if (expected_m < 0) return FP8GEMM_INVALID_ARG;
+  const int st = check_swiglu(A, sa, B, sb, Y, sy, M, I, K, G, masked_m, (long long)G * M * K,
+                              (long long)G * M * I);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  if (G > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
+  Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb, nullptr, M,
+         2 * I, K, G, masked_m, 0, 0, 1, K / BK, nullptr, static_cast<uint8_t *>(Y), sy};
+  return launch_tile<4, 2, 4, 4, 3, 4, MASKED, false, true>(a, G, static_cast<hipStream_t>(stream));
 }
 
 const char *fp8gemm_status_string(int status) {

@@ -21,7 +21,9 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = fg.declared_functions()
     assert set(names) == {"gemm_fp8_1x128_128x128_bf16", "grouped_contiguous",
-                          "grouped_masked", "quantize_fp8_1x128", "fp8gemm_status_string"}
+                          "grouped_masked", "quantize_fp8_1x128",
+                          "grouped_contiguous_swiglu_fp8", "grouped_masked_swiglu_fp8",
+                          "fp8gemm_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -89,6 +91,32 @@ def test_quantize_validation(lib):
     assert call(A=P_ODD) == MISALIGNED
     assert call(sa=ctypes.c_void_p(0x10002)) == MISALIGNED
     assert call(X=NUL, A=NUL, sa=NUL, M=0) == OK  # empty: nothing launched
+
+
+def test_swiglu_validation(lib):
+    def contig(G=2, M=256, I=256, K=256, Y=P, sy=P, idx=P):
+        return lib.grouped_contiguous_swiglu_fp8(P, P, P, P, Y, sy, M, I, K, G, NUL, idx)
+
+    def masked(G=2, M=256, I=256, K=256, Y=P, sy=P, mm=P, expected=64):
+        return lib.grouped_masked_swiglu_fp8(P, P, P, P, Y, sy, M, I, K, G, NUL, mm, expected)
+    for call in (contig, masked):
+        assert call(G=0) == INVALID
+        assert call(I=-128) == INVALID
+        assert call(sy=NUL) == INVALID
+        assert call(Y=NUL) == INVALID
+        assert call(I=64) == SHAPE      # I must be a whole number of 128-wide blocks
+        assert call(I=192) == SHAPE
+        assert call(K=20608) == SHAPE   # past the kernel's K range
+        assert call(K=100) == SHAPE
+        assert call(Y=P_ODD) == MISALIGNED
+        assert call(sy=ctypes.c_void_p(0x10002)) == MISALIGNED
+        assert call(M=0, Y=NUL, sy=NUL) == OK  # empty: nothing launched
+        assert call(I=0, Y=NUL, sy=NUL) == OK
+    assert contig(idx=NUL) == INVALID
+    assert contig(M=200) == SHAPE
+    assert masked(mm=NUL) == INVALID
+    assert masked(expected=-1) == INVALID
+    assert masked(G=1 << 16, M=1, K=128) == SHAPE
 
 
 def test_binding_rejects_bad_tensors():
