@@ -52,8 +52,9 @@ def _bind(lib):
     lib.fp8ref_swiglu_quant.restype = i32
     lib.fp8ref_points.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp,
                                   vp, vp, vp]
+    lib.fp8ref_gemm_bf16.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32]
     for f in (lib.fp8ref_gemm, lib.fp8ref_grouped_contiguous, lib.fp8ref_grouped_masked,
-              lib.fp8ref_points):
+              lib.fp8ref_points, lib.fp8ref_gemm_bf16):
         f.restype = i32
     return lib
 
@@ -212,3 +213,30 @@ def swiglu_quant(kind, A, sa, B, sb, idx, codes, scales, threads=None, lib=None)
         raise ValueError("fp8ref_swiglu_quant: bad arguments")
     return codes, scales
 
+
+
+def gemm_bf16(kind, A, B, idx=None, out=None, want64=False, threads=None, lib=None):
+    """BF16 NT GEMM without scales, D = bf16(A B^T) per row.  kind 'dense':
+    A [M,K], B [N,K]; 'contiguous': A [M,K], B [G,N,K], idx = m_indices [M];
+    'masked': A [G,M,K], B [G,N,K], idx = masked_m [G].  A and B hold bf16
+    bits (uint16).  `out` (bf16 bits, [M,N] or [G,M,N]) is updated in place:
+    rows not computed keep their contents.  Returns out (and the unrounded
+    fp64 values, NaN where not computed, with want64)."""
+    k = {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+    A, B = _c(A, np.uint16), _c(B, np.uint16)
+    if kind == "masked":
+        G, M, K = A.shape
+    else:
+        (M, K), G = A.shape, (B.shape[0] if kind == "contiguous" else 1)
+    N = B.shape[-2]
+    shape = (G, M, N) if kind == "masked" else (M, N)
+    if out is None:
+        out = np.zeros(shape, np.uint16)
+    assert out.shape == shape and out.dtype == np.uint16 and out.flags.c_contiguous
+    D64 = np.full(shape, np.nan) if want64 else None
+    ix = _c(idx, np.int32) if idx is not None else None
+    rc = (lib or load()).fp8ref_gemm_bf16(k, _p(A), _p(B), _p(out), _p(D64), M, N, K, G, _p(ix),
+                                          _threads(threads))
+    if rc:
+        raise ValueError("fp8ref_gemm_bf16: bad arguments")
+    return (out, D64) if want64 else out

@@ -1,6 +1,7 @@
 /*
  * fp8ref — the CPU oracle for the FP8 block-scaled NT GEMM and its two MoE
- * grouped layouts.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the
+ * grouped layouts, the 1x128 activation quantiser, the grouped GEMM with a
+ * fused SwiGLU, and the BF16 GEMM without scales.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the
  * benchmark's CPU-baseline leg use it; the product path never does.  It shares
  * no source with the GPU library.
  *
@@ -139,7 +140,10 @@ typedef struct {
   long row_begin, row_end; /* rows of the flattened output: dense/contig m, masked g*M+m */
   uint8_t *act;            /* SwiGLU form (N = 2I): codes [rows][I] and scales ... */
   float *act_scale;        /* ... [G or 1][I/128][M]; D and D64 unused */
+  const uint16_t *A16, *B16; /* BF16 form: bf16 operands, no scales (A, B, sa, sb unused) */
 } job_t;
+
+static void bf16_row(const job_t *j, long row);
 
 static void swiglu_row(const job_t *j, const uint8_t *A, const float *sa, const uint8_t *B,
                        const float *sb, long row, long m, long g);
@@ -188,7 +192,12 @@ static void do_row(const job_t *j, long row) {
 
 static void *worker(void *arg) {
   const job_t *j = (const job_t *)arg;
-  for (long r = j->row_begin; r < j->row_end; ++r) do_row(j, r);
+  for (long r = j->row_begin; r < j->row_end; ++r) {
+    if (j->A16)
+      bf16_row(j, r);
+    else
+      do_row(j, r);
+  }
   return NULL;
 }
 
@@ -423,3 +432,79 @@ int fp8ref_swiglu_quant(int kind, const uint8_t *A, const float *sa, const uint8
   return run(j, kind == MASKED ? (long)G * M : (long)M, threads);
 }
 
+
+/* ---- BF16 NT GEMM, no scales --------------------------------------------
+ * The pages list BF16 beside FP8 and FP4 among the library's number formats,
+ * with the same plain and grouped GEMM forms (kakushin, "Hva gjør
+ * DeepGEMM?", its first two items).  With no block scales the operation is
+ * the plain product
+ *   D[m,n] = bf16( sum_k A[m,k] * B[n,k] )
+ * A [M,K] and B [N,K] bf16 bits (K contiguous, "NT"), D [M,N] bf16 bits; the
+ * contiguous and masked layouts are the FP8 calls' without their scales
+ * (B [G,N,K]; masked A [G,M,K] and D [G,M,N]), with the same row rules.
+ * Every product of two bf16 values is exact in fp64 (8-bit significands);
+ * the sum runs over k ascending in fp64, then one rounding to bf16 as
+ * above.  Any K >= 0 is accepted (K = 0 gives zeros). */
+static double bf16_val(uint16_t b) { return (double)bf16_to_float(b); }
+
+static double bf16_dot(const uint16_t *a, const uint16_t *b, long K) {
+  double s = 0.0;
+#if MUTANT == 10 /* planted mistake: the last product of the sum dropped */
+  for (long k = 0; k + 1 < K; ++k) s += bf16_val(a[k]) * bf16_val(b[k]);
+#else
+  for (long k = 0; k < K; ++k) s += bf16_val(a[k]) * bf16_val(b[k]);
+#endif
+  return s;
+}
+
+static void bf16_row(const job_t *j, long row) {
+  const long M = j->M, N = j->N, K = j->K;
+  const uint16_t *A = j->A16, *B = j->B16;
+  long m = row;
+  if (j->kind == CONTIG) {
+    const int g = j->m_indices[row];
+    if (g < 0 || g >= j->G) return; /* padding row: untouched */
+    B += (long)g * N * K;
+  } else if (j->kind == MASKED) {
+    const long g = row / M;
+    m = row % M;
+    int valid = j->masked_m[g];
+    if (valid < 0) valid = 0;
+    if (valid > j->M) valid = j->M;
+    if (m >= valid) return; /* masked row: untouched */
+    A += g * M * K;
+    B += g * N * K;
+  }
+  for (long n = 0; n < N; ++n) {
+#if MUTANT == 11 /* planted mistake: B read as if stored [K][N] */
+    double v = 0.0;
+    for (long k = 0; k < K; ++k) v += bf16_val(A[m * K + k]) * bf16_val(B[k * N + n]);
+#else
+    const double v = bf16_dot(A + m * K, B + n * K, K);
+#endif
+    if (j->D) j->D[row * N + n] = fp8ref_bf16_rne(v);
+    if (j->D64) j->D64[row * N + n] = v;
+  }
+}
+
+/* kind: 0 dense (G = 1, idx unused), 1 contiguous (idx = m_indices [M]),
+ * 2 masked (idx = masked_m [G]).  D / D64 nullable as in fp8ref_gemm. */
+int fp8ref_gemm_bf16(int kind, const uint16_t *A, const uint16_t *B, uint16_t *D, double *D64,
+                     int M, int N, int K, int G, const int32_t *idx, int threads) {
+  if (M < 0 || N < 0 || K < 0 || G < 1 || kind < DENSE || kind > MASKED) return 1;
+  if (kind != DENSE && !idx) return 1;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.kind = kind;
+  j.A16 = A;
+  j.B16 = B;
+  j.D = D;
+  j.D64 = D64;
+  j.M = M;
+  j.N = N;
+  j.K = K;
+  j.G = kind == DENSE ? 1 : G;
+  j.m_indices = kind == CONTIG ? idx : NULL;
+  j.masked_m = kind == MASKED ? idx : NULL;
+  return run(j, kind == MASKED ? (long)G * M : (long)M, threads);
+}

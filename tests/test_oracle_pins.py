@@ -545,6 +545,70 @@ def test_swiglu_quant_masked_rows_and_zero_gate():
     assert (codes[0, :3] == c).all() and (scales[0, :, :3] == sc).all()
 
 
+# ------------------------------------------------------------- BF16 GEMM ----
+
+
+def rand_bf16(rng, shape, scale=1.0):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 values will do
+
+
+def bf16_exact_bits(A, B):
+    """D = bf16(A B^T) by exact rationals (tiny sizes only)."""
+    fa = [[Fraction(float(v)) for v in row] for row in bits_to_f32(A)]
+    fb = [[Fraction(float(v)) for v in row] for row in bits_to_f32(B)]
+    return np.array([[exact_bf16_bits(sum((x * y for x, y in zip(ra, rb)), Fraction(0)))
+                      for rb in fb] for ra in fa], np.uint16).reshape(len(fa), len(fb))
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(3, 5, 64, 1), (2, 3, 7, 2), (4, 4, 130, 3)])
+def test_bf16_gemm_exact_rational(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    A, B = rand_bf16(rng, (M, K)), rand_bf16(rng, (N, K), 4.0)
+    assert (oracle.gemm_bf16("dense", A, B) == bf16_exact_bits(A, B)).all()
+
+
+def test_bf16_gemm_matches_numpy_float64_matmul():
+    """a library matmul of the decoded values; products of bf16 values are
+    exact in fp64 and these sums stay exact, so the bits agree"""
+    rng = np.random.default_rng(11)
+    A, B = rand_bf16(rng, (40, 256)), rand_bf16(rng, (24, 256))
+    ref = bits_to_f32(A).astype(np.float64) @ bits_to_f32(B).astype(np.float64).T
+    want = np.array([oracle.bf16_rne(v) for v in ref.ravel()], np.uint16).reshape(ref.shape)
+    got, d64 = oracle.gemm_bf16("dense", A, B, want64=True)
+    assert (got == want).all()
+    assert np.array_equal(d64, ref)
+
+
+def test_bf16_identity_and_zero_k():
+    rng = np.random.default_rng(12)
+    B = rand_bf16(rng, (6, 64))
+    eye = np.zeros((64, 64), np.uint16)
+    eye[np.arange(64), np.arange(64)] = 0x3F80  # 1.0
+    assert (oracle.gemm_bf16("dense", eye, B) == B.T).all()  # bf16 values pass through exactly
+    D = oracle.gemm_bf16("dense", np.zeros((3, 0), np.uint16), np.zeros((2, 0), np.uint16))
+    assert (D == 0).all()
+
+
+def test_bf16_grouped_rows():
+    rng = np.random.default_rng(13)
+    G, M, N, K = 3, 8, 5, 64
+    A, B = rand_bf16(rng, (M, K)), rand_bf16(rng, (G, N, K))
+    idx = np.array([0, 2, -1, 1, 7, 1, 0, -4], np.int32)
+    D = oracle.gemm_bf16("contiguous", A, B, idx, out=np.full((M, N), 0x7FBF, np.uint16))
+    for m, g in enumerate(idx):
+        if 0 <= g < G:
+            assert (D[m] == oracle.gemm_bf16("dense", A[m:m + 1], B[g])[0]).all()
+        else:
+            assert (D[m] == 0x7FBF).all()
+    Am = rand_bf16(rng, (G, M, K))
+    mm = np.array([8, 0, 30], np.int32)  # full, empty, clamped to M
+    Dm = oracle.gemm_bf16("masked", Am, B, mm, out=np.full((G, M, N), 0x7FBF, np.uint16))
+    assert (Dm[0] == oracle.gemm_bf16("dense", Am[0], B[0])).all()
+    assert (Dm[1] == 0x7FBF).all()
+    assert (Dm[2] == oracle.gemm_bf16("dense", Am[2], B[2])).all()
+
+
 # ------------------------------------------------------ planted mistakes ----
 
 MUTANTS = {
@@ -557,6 +621,8 @@ MUTANTS = {
     7: "rounds e4m3 ties towards the larger code",
     8: "quantises with scale amax / 447",
     9: "swaps the gate and up halves of the SwiGLU",
+    10: "drops the last product of a BF16 dot product",
+    11: "reads the BF16 weights as [K][N]",
 }
 
 
@@ -604,6 +670,10 @@ def _pins_pass(lib):
     ci, si = independent_swiglu_quant(A3, sa3, B3[0], sb3[0])
     if not ((c3 == ci).all() and (s3 == si).all()):
         failed.append("swiglu")
+    # BF16 GEMM: exact rationals on a tiny problem
+    A4, B4 = rand_bf16(rng, (2, 6)), rand_bf16(rng, (3, 6))
+    if not (oracle.gemm_bf16("dense", A4, B4, lib=lib) == bf16_exact_bits(A4, B4)).all():
+        failed.append("bf16_exact")
     return failed
 
 
