@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "FP8 block-scaled GEMM TFLOPS & % of FP8 MFMA peak (HBM GB/s for small M)"
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0  # dense FP8 MFMA, MI355X published figure
+PEAK_BF16_TFLOPS = 2500.0  # dense BF16 MFMA, MI355X published figure
 ROTATE_BYTES = 1 << 30
 
 
@@ -55,6 +56,10 @@ class Call:
         self.kind, self.d, self.label, self.flop, self.bytes = kind, d, label, flop, by
 
     def to_device(self, torch, dev):
+        if self.kind == "bf16":
+            t = {k: torch.from_numpy(self.d[k].view("int16")).view(torch.bfloat16).to(dev) for k in ("A", "B")}
+            t["D"] = torch.empty((self.d["M"], self.d["N"]), dtype=torch.bfloat16, device=dev)
+            return t
         if self.kind == "quant":
             X = torch.from_numpy(self.d["X"].view("int16")).view(torch.bfloat16).to(dev)
             M, K = self.d["M"], self.d["K"]
@@ -74,7 +79,9 @@ class Call:
         return t
 
     def launch(self, fg, t):
-        if self.kind == "quant":
+        if self.kind == "bf16":
+            fg.gemm_bf16_nt(t["A"], t["B"], t["D"])
+        elif self.kind == "quant":
             fg.quantize_fp8_1x128(t["X"], t["A"], t["sa"])
         elif self.kind == "dense":
             fg.gemm_fp8_1x128_128x128_bf16(t["A"], t["sa"], t["B"], t["sb"], t["D"])
@@ -115,6 +122,16 @@ def workload_calls(name):
             xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
             d = {"X": xb, "M": M, "K": K}
             calls.append(Call("quant", d, f"quantize {M}x{K}", 0.0, 3 * M * K + 4 * M * (K // 128)))
+    elif name == "bf16":
+        import torch
+        import synth
+        for i, (M, N, K) in enumerate(W.PREFILL_SHAPES):
+            def b16(seed, shape, scale):
+                x = synth.normal(seed, shape[0] * shape[1]).reshape(shape) * scale
+                return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            d = {"A": b16(7000 + 10 * i, (M, K), 1.0), "B": b16(7001 + 10 * i, (N, K), 0.5),
+                 "M": M, "N": N, "K": K}
+            calls.append(Call("bf16", d, f"bf16 {M}x{N}x{K}", 2.0 * M * N * K, 2 * (M * K + N * K + M * N)))
     elif name == "swiglu":
         # the experts' gate/up projection (N = 2I = 4096, K = 7168) with the
         # SwiGLU and 1x128 requantisation fused: codes [rows, I] and scales
@@ -148,6 +165,7 @@ WORKLOAD_TEXT = {
     "contiguous": "MoE grouped FP8 GEMM, M-axis contiguous: G=4 x 8192 rows and G=8 uneven (32768 padded rows), N=4096, K=7168",
     "masked": "MoE grouped FP8 GEMM, masked: G=16, 256 rows/expert, masked_m ~ U[0,256], (N,K) in {(4096,7168),(7168,2048)}",
     "swiglu": "MoE gate/up projection with SwiGLU and 1x128 FP8 requantisation fused: contiguous G=4 x 8192 rows and G=8 uneven (32768 padded rows), masked G=16 x 256 rows; N=2I=4096, K=7168",
+    "bf16": "dense BF16 GEMM without scales (fp32 accumulate, bf16 out), M=4096 x (N,K) in {(7168,16384),(2112,7168),(24576,1536),(7168,18432)}",
     "quant": "1x128 FP8 quantisation of bf16 activations, M=4096 x K in {16384,7168,1536,18432} (the prefill A operands), 1% rows x50",
 }
 MEMORY_BOUND = {"decode", "small", "masked", "quant"}
@@ -269,8 +287,9 @@ def main():
         roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dom["GBps"] / PEAK_HBM_GBS, "traffic": None}
     else:
-        roof = {"bound": "mfma", "achieved": dom["TFLOPS"], "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom["TFLOPS"] / PEAK_FP8_TFLOPS, "traffic": None}
+        peak = PEAK_BF16_TFLOPS if args.workload == "bf16" else PEAK_FP8_TFLOPS
+        roof = {"bound": "mfma", "achieved": dom["TFLOPS"], "peak": peak,
+                "unit": "TFLOP/s", "frac": dom["TFLOPS"] / peak, "traffic": None}
     roof["kernel"] = dom["call"]
     roof["avg_us"] = dom["avg_us"]
     roof["traffic"] = measured_traffic(roof["kernel"])
@@ -286,11 +305,13 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
+        "dtype": "bf16 (fp32 accumulate)" if args.workload == "bf16" else "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "calls": len(calls),
                    "rotating_copies": copies, "parallelism": "none (1 GPU)"},
         "tflops": tflops,
         "frac_fp8_peak": tflops / PEAK_FP8_TFLOPS,
+        "frac_mfma_peak": tflops / (PEAK_BF16_TFLOPS if args.workload == "bf16" else PEAK_FP8_TFLOPS),
         "gbps": gbps,
         "frac_hbm_peak": gbps / PEAK_HBM_GBS,
         "per_call": per_call,
@@ -492,6 +513,20 @@ def cpu_baseline(calls, budget_s, memory_bound):
                 if passes == 0:
                     done.append(f"quantize {rows}x{K}")
                 by += 3 * rows * K + 4 * rows * (K // 128)
+                if time.perf_counter() - t0 > budget_s:
+                    break
+                continue
+            if c.kind == "bf16":
+                A, B = d["A"], d["B"]
+                M, K = A.shape
+                N = B.shape[0]
+                left = max(0.2, budget_s - (time.perf_counter() - t0))
+                rows = max(1, min(M, int(left * 3e8 * threads / (N * K))))
+                oracle.gemm_bf16("dense", A[:rows], B, threads=threads)
+                if passes == 0:
+                    done.append(f"{rows}x{N}x{K}")
+                by += 2 * (rows * K + N * K + rows * N)
+                fl += 2.0 * rows * N * K
                 if time.perf_counter() - t0 > budget_s:
                     break
                 continue

@@ -166,6 +166,30 @@ int grouped_masked_swiglu_fp8(const void *A, const float *sa, const void *B, con
                               void *Y, float *sy, int M, int I, int K, int G, void *stream,
                               const int32_t *masked_m, int expected_m);
 
+/*
+ * BF16 NT GEMM without scales: the pages list BF16 beside FP8 among the
+ * library's number formats, with the same plain and grouped GEMM forms
+ * (kakushin.no, "Hva gjør DeepGEMM?", its first two items).
+ *   D[m,n] = bf16( sum_k A[m,k] * B[n,k] ), fp32 accumulation in the MFMA.
+ * A, B and D hold bf16 bit patterns (2 bytes each), row-major, K contiguous
+ * in A and B.  Layouts and row rules are those of the FP8 calls above with
+ * the scales removed: dense A [M,K], B [N,K], D [M,N]; contiguous adds
+ * B [G][N,K] and m_indices [M]; masked has A [G][M,K], B [G][N,K],
+ * D [G][M,N] and masked_m [G].  Conventions as above (device pointers,
+ * asynchronous on `stream`, errors before any launch, the same workspace
+ * rule for the dense call with M <= 128).
+ * Constraints: K % 64 == 0 (FP8GEMM_UNSUPPORTED_SHAPE otherwise); every
+ * tensor below 2^31 bytes; A, B and D 16-byte aligned.  M == 0 or N == 0
+ * returns FP8GEMM_OK without launching; K == 0 writes zeros.
+ */
+int gemm_bf16_nt(const void *A, const void *B, void *D, int M, int N, int K, void *stream);
+
+int grouped_contiguous_bf16(const void *A, const void *B, void *D, int M, int N, int K, int G,
+                            void *stream, const int32_t *m_indices);
+
+int grouped_masked_bf16(const void *A, const void *B, void *D, int M, int N, int K, int G,
+                        void *stream, const int32_t *masked_m, int expected_m);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fp8gemm_status_string(int status);
 

@@ -25,6 +25,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8gemm.h")
 
 __all__ = ["gemm_fp8_1x128_128x128_bf16", "grouped_contiguous", "grouped_masked",
            "quantize_fp8_1x128", "grouped_contiguous_swiglu_fp8", "grouped_masked_swiglu_fp8",
+           "gemm_bf16_nt", "grouped_contiguous_bf16", "grouped_masked_bf16",
            "fp8gemm_status_string", "Fp8GemmError", "load_library",
            "LIB_PATH"]
 
@@ -54,9 +55,13 @@ def load_library():
                                                       vp, vp]
         lib.grouped_masked_swiglu_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
                                                   vp, i32]
+        lib.gemm_bf16_nt.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        lib.grouped_contiguous_bf16.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+        lib.grouped_masked_bf16.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32]
         for f in (lib.gemm_fp8_1x128_128x128_bf16, lib.grouped_contiguous, lib.grouped_masked,
                   lib.quantize_fp8_1x128, lib.grouped_contiguous_swiglu_fp8,
-                  lib.grouped_masked_swiglu_fp8):
+                  lib.grouped_masked_swiglu_fp8, lib.gemm_bf16_nt, lib.grouped_contiguous_bf16,
+                  lib.grouped_masked_bf16):
             f.restype = i32
         lib.fp8gemm_status_string.argtypes = [i32]
         lib.fp8gemm_status_string.restype = ctypes.c_char_p
@@ -253,3 +258,61 @@ def grouped_masked_swiglu_fp8(A, sa, B, sb, masked_m, expected_m, Y=None, sy=Non
         _p(A), _p(sa), _p(B), _p(sb), _p(Y), _p(sy), M, I, K, G, _stream(stream, dev),
         _p(masked_m), int(expected_m)))
     return Y, sy
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    return t
+
+
+def gemm_bf16_nt(A, B, D=None, stream=None):
+    """D[M,N] = bf16(A[M,K] B[N,K]^T), all bfloat16, fp32 accumulation; returns D."""
+    A, B = _bf16(A, "A"), _bf16(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if D is None:
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _shape(B, (N, K), "B")
+    _shape(_bf16(D, "D"), (M, N), "D")
+    dev = _dev(A, B, D)
+    _check(load_library().gemm_bf16_nt(_p(A), _p(B), _p(D), M, N, K, _stream(stream, dev)))
+    return D
+
+
+def grouped_contiguous_bf16(A, B, m_indices, D=None, stream=None):
+    """BF16 contiguous grouping: A [M,K], B [G,N,K], m_indices [M] int32;
+    rows whose index is outside [0,G) are not written.  Returns D [M,N]."""
+    A, B = _bf16(A, "A"), _bf16(B, "B")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    if D is None:
+        D = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _shape(B, (G, N, K), "B")
+    _shape(m_indices, (M,), "m_indices")
+    _shape(_bf16(D, "D"), (M, N), "D")
+    if m_indices.dtype != torch.int32:
+        raise TypeError("m_indices must be int32")
+    dev = _dev(A, B, m_indices, D)
+    _check(load_library().grouped_contiguous_bf16(_p(A), _p(B), _p(D), M, N, K, G,
+                                                  _stream(stream, dev), _p(m_indices)))
+    return D
+
+
+def grouped_masked_bf16(A, B, masked_m, expected_m, D=None, stream=None):
+    """BF16 masked grouping: A [G,M,K], B [G,N,K], masked_m [G] int32; only
+    rows m < masked_m[g] of D [G,M,N] are written.  Returns D."""
+    A, B = _bf16(A, "A"), _bf16(B, "B")
+    G, M, K = A.shape
+    N = B.shape[1]
+    if D is None:
+        D = torch.empty((G, M, N), dtype=torch.bfloat16, device=A.device)
+    _shape(B, (G, N, K), "B")
+    _shape(masked_m, (G,), "masked_m")
+    _shape(_bf16(D, "D"), (G, M, N), "D")
+    if masked_m.dtype != torch.int32:
+        raise TypeError("masked_m must be int32")
+    dev = _dev(A, B, masked_m, D)
+    _check(load_library().grouped_masked_bf16(_p(A), _p(B), _p(D), M, N, K, G,
+                                              _stream(stream, dev), _p(masked_m), int(expected_m)))
+    return D

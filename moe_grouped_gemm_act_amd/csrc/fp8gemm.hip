@@ -92,6 +92,15 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// chunk h (0: first 16 bytes, 1: second) of a fragment as 8 bf16 values
+__device__ __forceinline__ bf16x8 bf_half(const v8i &v, int h) {
+  const u32x4 x = h ? u32x4{(unsigned)v[4], (unsigned)v[5], (unsigned)v[6], (unsigned)v[7]}
+                    : u32x4{(unsigned)v[0], (unsigned)v[1], (unsigned)v[2], (unsigned)v[3]};
+  return __builtin_bit_cast(bf16x8, x);
+}
+
 __device__ __forceinline__ v8i frag(const uint8_t *row_ptr, int row, int g) {
   u32x4 lo = *reinterpret_cast<const u32x4 *>(row_ptr + chunk_pos(g, row));
   u32x4 hi = *reinterpret_cast<const u32x4 *>(row_ptr + chunk_pos(g + 4, row));
@@ -318,15 +327,17 @@ __device__ __forceinline__ int fresh_lane_id() {
   return l;
 }
 
-template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, bool ACT, int LAYOUT>
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, bool ACT, int LAYOUT,
+          bool BF = false>
 __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   constexpr int ROWS = BM + BN;
-  constexpr int SLOT = ROWS * BK + BM * 4;  // operand rows, then the BM activation scales
+  // BF: bf16 operands with no scales; a "K block" is then 128 bytes = 64 elements
+  constexpr int SLOT = ROWS * BK + (BF ? 0 : BM * 4);  // operand rows, then the BM activation scales
   constexpr int OCT = ROWS / 8;             // 1 KB row groups per slot
   constexpr int DMA = OCT / NLD;            // row-group loads per loader wave per slot
   constexpr int SG = BM / 64;               // 64-float activation-scale loads per slot
-  constexpr int SPL = (SG + NLD - 1) / NLD; // of which per loader (spares repeat one: same bytes, same place)
+  constexpr int SPL = BF ? 0 : (SG + NLD - 1) / NLD; // of which per loader (spares repeat one: same bytes, same place)
   constexpr int PER_G = DMA + SPL;          // vector memory instructions per loader per slot
   constexpr int MAXKB = 160;                // K <= 20480 for the weight-scale preload
   constexpr int NCW = WGN * WGM;            // compute waves
@@ -337,15 +348,17 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   // ACT (fused SwiGLU): the tile's weight rows are 128 gate rows (waves
   // wn < WGN/2) and the 128 matching up rows; its output is 128 columns of y
   static_assert(!ACT || (BN == 256 && WGN == 4 && TN == 4 && BM <= 128), "SwiGLU tile shape");
+  static_assert(!(ACT && BF), "the fused SwiGLU takes FP8 operands");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
-  __shared__ float s_sb[BN > 128 ? 2 : 1][MAXKB];
+  __shared__ float s_sb[BN > 128 ? 2 : 1][BF ? 1 : MAXKB];
   __shared__ float s_rmax[ACT ? 2 : 1][ACT ? BM : 1];  // ACT: row maxima of y per gate wave column
   __shared__ int s_group;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fg = lane >> 4;
-  const int M = a.M, N = a.N, K = a.K, Kb = K / BK, Nb = (N + 127) / 128;
+  const int M = a.M, N = a.N, K = a.K, Nb = (N + 127) / 128;
+  const int RB = BF ? 2 * K : K, Kb = RB / BK;  // operand row bytes, K blocks
 
   // work order: workgroup ids are dealt to the 8 XCDs round robin; give each
   // XCD a contiguous run of (split, tile) items, walked GROUPN weight tiles
@@ -380,8 +393,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     const int c = a.idx[g];
     mvalid = c < 0 ? 0 : (c > M ? M : c);
     if (m0 >= mvalid) return;  // whole tile masked: nothing loaded, nothing written
-    A += (size_t)g * M * K;
-    sa += (size_t)g * Kb * M;
+    A += (size_t)g * M * RB;
+    if (!BF) sa += (size_t)g * Kb * M;
     D += (size_t)g * M * N;
     act += (size_t)g * M * (N / 2);
     act_scale += (size_t)g * (N / 256) * M;
@@ -398,8 +411,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     if (g < 0) return;  // all padding
   }
   if (LAYOUT != DENSE) {
-    B += (size_t)g * N * K;
-    sb += (size_t)g * Nb * Kb;
+    B += (size_t)g * N * RB;
+    if (!BF) sb += (size_t)g * Nb * Kb;
   }
   if (wave >= NCW) {
     // ---------------- loader waves ----------------
@@ -407,8 +420,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     const int lane = ACT ? fresh_lane_id() : tid & 63;
     constexpr int QA = BM / 8 / NLD;  // loads q < QA are activation row groups, the rest weights
     static_assert((BM / 8) % NLD == 0, "row groups split evenly between A and B");
-    const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint32_t)M * K);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(B, (uint32_t)N * K);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(A, (uint32_t)M * RB);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(B, (uint32_t)N * RB);
     const __amdgpu_buffer_rsrc_t rs = rsrc(sa, (uint32_t)M * Kb * 4);
     // q-th row-group load: rows (L + NLD q) * 8 .. + 7 of the slot; lane l ->
     // row + l / 8, physical chunk l % 8 holding logical chunk (l % 8) ^ key(row).
@@ -420,16 +433,16 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
       const int r = (L + NLD * q) * 8 + (lane >> 3);
       const int col = (lane & 7) ^ row_key(r);
       if (q < QA) {
-        off[q] = m0 + r < mvalid ? (uint32_t)(m0 + r) * K + col * 16 : OOB;
+        off[q] = m0 + r < mvalid ? (uint32_t)(m0 + r) * RB + col * 16 : OOB;
       } else {
         const int rw = r - BM;  // weight row of the tile
         // ACT: gate rows 128 tn + rw, then up rows N/2 + 128 tn + (rw - 128)
         const int grow = ACT ? (rw < 128 ? tn * 128 + rw : N / 2 + tn * 128 + rw - 128) : n0 + rw;
-        off[q] = grow < N ? (uint32_t)grow * K + col * 16 : OOB;
+        off[q] = grow < N ? (uint32_t)grow * RB + col * 16 : OOB;
       }
     }
-    uint32_t soff[SPL];  // byte offsets of scale floats 64 j + lane of the tile's rows
-    int sdst[SPL];
+    uint32_t soff[SPL > 0 ? SPL : 1];  // byte offsets of scale floats 64 j + lane of the tile's rows
+    int sdst[SPL > 0 ? SPL : 1];
 #pragma unroll
     for (int jj = 0; jj < SPL; ++jj) {
       const int j = (L + NLD * jj) % SG;
@@ -483,85 +496,125 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  // the weight scales of the K range go to LDS while the loaders start; the
-  // first K-block barrier publishes them
-  for (int i = tid; i < (BN > 128 ? 2 : 1) * nk; i += CT) {
-    const int h = i / nk, t = i % nk;
-    const int blk = ACT ? (h == 0 ? tn : N / 256 + tn) : min(n0 / 128 + h, Nb - 1);
-    s_sb[h][t] = sb[(size_t)blk * Kb + kb0 + t];
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // Product k = j * TN + i of a K block (activation group j, weight group i)
-  // comes from one MFMA; it is promoted LAG MFMAs later, when it has long
-  // landed, so the promotion FMAs issue in the shadow of the next MFMAs
-  // instead of waiting on the one just issued.  Products sit in a ring of
-  // RING registers; TN * TM is a multiple of RING, so slots and the promotion
-  // of the previous block's last products line up across blocks.  The next
-  // activation fragment and its scale are read from LDS one group ahead.
-  constexpr int LAG = 2, RING = 4;
-  static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
-  v4f ring[RING];
+  if constexpr (BF) {
+    // BF16: no scales, so products accumulate straight in the MFMA's own
+    // accumulator.  A lane's two 16-byte chunks of a 128-byte block row hold
+    // elements 8g..8g+7 and 32+8g..32+8g+7 (g = lane / 16): exactly the
+    // operands of two 16x16x32 bf16 MFMAs, over the block's first and second
+    // 32 elements.  All sub-tiles take the first half before the second, so
+    // no MFMA waits on the one just issued.
+    for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
-  for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
-  float sc_last = 0.f;  // scale of the previous block's last activation group
-  for (int t0 = 0; t0 < nk; t0 += STAGES) {
-#pragma unroll
-    for (int u = 0; u < STAGES; ++u) {
-      const int t = t0 + u;
-      if (t >= nk) break;
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();  // block t is in slot u
-      asm volatile("" ::: "memory");
-      // ACT: the slot's offset goes through an empty asm, so the compiler
-      // adds it at each read instead of keeping every slot's fragment
-      // addresses in registers through the loop
-      int so = u * SLOT;
-      if (ACT) asm volatile("" : "+s"(so));
-      const uint8_t *sl = &lds[0][0] + so;
-      const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
-      const float sbv = s_sb[hsb][t];
-      v8i bfr[TN], afr[2];
-      float scb[TM];
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        const int row = BM + (wn * TN + i) * 16 + fr;
-        bfr[i] = frag(sl + row * BK, row, fg);
-      }
-      {
-        const int row = wm * TM * 16 + fr;
-        afr[0] = frag(sl + row * BK, row, fg);
-        scb[0] = ssl[row] * sbv;
-      }
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (j + 1 < TM) {
-          const int row = (wm * TM + j + 1) * 16 + fr;
-          afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
-          scb[j + 1] = ssl[row] * sbv;
-        }
+      for (int u = 0; u < STAGES; ++u) {
+        const int t = t0 + u;
+        if (t >= nk) break;
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // block t is in slot u
+        asm volatile("" ::: "memory");
+        const uint8_t *sl = lds[u];
+        v8i bfr[TN], afr[TM];
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
-          const int k = j * TN + i;
-          ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-          const int kp = k - LAG;                      // product promoted now
-          const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
-          const float sp = kp >= 0 ? scb[kq / TN] : sc_last;
-          v4f &ap = acc[kq % TN][kq / TN];
-          const v4f &pp = ring[(kq + RING) % RING];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ap[r] = __builtin_fmaf(pp[r], sp, ap[r]);
+          const int row = BM + (wn * TN + i) * 16 + fr;
+          bfr[i] = frag(sl + row * BK, row, fg);
         }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const int row = (wm * TM + j) * 16 + fr;
+          afr[j] = frag(sl + row * BK, row, fg);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_half(bfr[i], h),
+                                                                  bf_half(afr[j], h), acc[i][j],
+                                                                  0, 0, 0);
       }
-      sc_last = scb[TM - 1];
     }
+  } else {
+    // the weight scales of the K range go to LDS while the loaders start; the
+    // first K-block barrier publishes them
+    for (int i = tid; i < (BN > 128 ? 2 : 1) * nk; i += CT) {
+      const int h = i / nk, t = i % nk;
+      const int blk = ACT ? (h == 0 ? tn : N / 256 + tn) : min(n0 / 128 + h, Nb - 1);
+      s_sb[h][t] = sb[(size_t)blk * Kb + kb0 + t];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // Product k = j * TN + i of a K block (activation group j, weight group i)
+    // comes from one MFMA; it is promoted LAG MFMAs later, when it has long
+    // landed, so the promotion FMAs issue in the shadow of the next MFMAs
+    // instead of waiting on the one just issued.  Products sit in a ring of
+    // RING registers; TN * TM is a multiple of RING, so slots and the promotion
+    // of the previous block's last products line up across blocks.  The next
+    // activation fragment and its scale are read from LDS one group ahead.
+    constexpr int LAG = 2, RING = 4;
+    static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
+    v4f ring[RING];
+#pragma unroll
+    for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
+    float sc_last = 0.f;  // scale of the previous block's last activation group
+    for (int t0 = 0; t0 < nk; t0 += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) {
+        const int t = t0 + u;
+        if (t >= nk) break;
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // block t is in slot u
+        asm volatile("" ::: "memory");
+        // ACT: the slot's offset goes through an empty asm, so the compiler
+        // adds it at each read instead of keeping every slot's fragment
+        // addresses in registers through the loop
+        int so = u * SLOT;
+        if (ACT) asm volatile("" : "+s"(so));
+        const uint8_t *sl = &lds[0][0] + so;
+        const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
+        const float sbv = s_sb[hsb][t];
+        v8i bfr[TN], afr[2];
+        float scb[TM];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int row = BM + (wn * TN + i) * 16 + fr;
+          bfr[i] = frag(sl + row * BK, row, fg);
+        }
+        {
+          const int row = wm * TM * 16 + fr;
+          afr[0] = frag(sl + row * BK, row, fg);
+          scb[0] = ssl[row] * sbv;
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          if (j + 1 < TM) {
+            const int row = (wm * TM + j + 1) * 16 + fr;
+            afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
+            scb[j + 1] = ssl[row] * sbv;
+          }
+#pragma unroll
+          for (int i = 0; i < TN; ++i) {
+            const int k = j * TN + i;
+            ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            const int kp = k - LAG;                      // product promoted now
+            const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
+            const float sp = kp >= 0 ? scb[kq / TN] : sc_last;
+            v4f &ap = acc[kq % TN][kq / TN];
+            const v4f &pp = ring[(kq + RING) % RING];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ap[r] = __builtin_fmaf(pp[r], sp, ap[r]);
+          }
+        }
+        sc_last = scb[TM - 1];
+      }
+    }
+#pragma unroll
+    for (int k = TN * TM - LAG; k < TN * TM; ++k)  // the last block's last products
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
   }
-#pragma unroll
-  for (int k = TN * TM - LAG; k < TN * TM; ++k)  // the last block's last products
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
 
   if constexpr (ACT) {
     // Fused SwiGLU and 1x128 requantisation of y = silu(g) u.  Gate values sit
@@ -756,17 +809,18 @@ const Workspace *workspace(hipStream_t s) {
 }
 
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool KSPLIT = false,
-          bool ACT = false>
+          bool ACT = false, bool BF = false>
 int launch_tile(Args a, int groups, hipStream_t stream) {
   a.tiles_m = cdiv(a.M, WGM * TM * 16);
   a.tiles_n = cdiv(a.N, WGN * TN * 16);
   if (!KSPLIT) {
     a.splits = 1;
-    a.kb_per_split = a.K / BK;
+    a.kb_per_split = (BF ? 2 * a.K : a.K) / BK;
   }
   void *kargs[] = {&a};
   hipError_t e = hipLaunchKernel(
-      reinterpret_cast<const void *>(&tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, KSPLIT, ACT, LAYOUT>),
+      reinterpret_cast<const void *>(
+          &tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, KSPLIT, ACT, LAYOUT, BF>),
       dim3(a.tiles_m * a.tiles_n * a.splits, groups), dim3((WGN * WGM + NLD) * 64), kargs, 0,
       stream);
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
@@ -793,23 +847,25 @@ bool decode_built(int bn, int stages, int bm) {
 // byte); a K split only when the tiles alone leave CUs idle, with (tiles x
 // splits) kept within one wave of 256 workgroups and at least 9 K blocks per
 // split, since the partial planes and their reduction cost about 3 us.
-DecodeCfg decode_config(int M, int N, int K) {
+DecodeCfg decode_config(int M, int N, int Kb) {
   const int bm = M <= 64 ? 64 : 128;
   const char *e = getenv("FP8GEMM_DECODE");
   DecodeCfg o;
   if (e && sscanf(e, "%d,%d,%d", &o.bn, &o.stages, &o.splits) == 3 && o.splits >= 1 &&
       decode_built(o.bn, o.stages, bm))
     return o;
-  const int Kb = K / BK, tiles64 = cdiv(N, 64);
+  const int tiles64 = cdiv(N, 64);
   DecodeCfg c{tiles64 >= 384 ? 128 : 64, 4, 1};
   const int tiles = cdiv(N, c.bn) * cdiv(M, bm);
   c.splits = std::max(1, std::min(256 / std::max(tiles, 1), Kb / 9));
   return c;
 }
 
+// BF: bf16 operands, K blocks of 64 elements (128 bytes)
+template <bool BF>
 int run_decode(Args a, hipStream_t stream) {
-  DecodeCfg c = decode_config(a.M, a.N, a.K);
-  const int Kb = a.K / BK;
+  const int Kb = (BF ? 2 * a.K : a.K) / BK;
+  DecodeCfg c = decode_config(a.M, a.N, Kb);
   const int bm = a.M <= 64 ? 64 : 128;
   int splits = std::max(1, std::min(c.splits, std::max(Kb, 1)));
   const int kps = Kb > 0 ? cdiv(Kb, splits) : 0;
@@ -828,8 +884,8 @@ int run_decode(Args a, hipStream_t stream) {
   int st = FP8GEMM_LAUNCH_FAILED;  // unreachable: decode_config returns built instances only
 #define DEC(BN_, ST_)                                                                     \
   if (c.bn == BN_ && c.stages == ST_)                                                     \
-    st = bm == 64 ? launch_tile<1, 4, BN_ / 16, 1, ST_, 4, DENSE, true>(a, 1, stream)      \
-                  : launch_tile<1, 4, BN_ / 16, 2, ST_, 4, DENSE, true>(a, 1, stream);
+    st = bm == 64 ? launch_tile<1, 4, BN_ / 16, 1, ST_, 4, DENSE, true, false, BF>(a, 1, stream) \
+                  : launch_tile<1, 4, BN_ / 16, 2, ST_, 4, DENSE, true, false, BF>(a, 1, stream);
   DEC(64, 4)
   DEC(64, 6)
   DEC(128, 4)
@@ -881,7 +937,7 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, K / BK, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= 128 && K <= 20480) return run_decode(a, s);
+  if (M <= 128 && K <= 20480) return run_decode<false>(a, s);
   if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
   // 256 activation rows x 128 weight rows, eight compute waves (two per
   // SIMD, so one wave's promotion FMAs run under the other's MFMAs) and four
@@ -970,6 +1026,63 @@ int grouped_masked_swiglu_fp8(const void *A, const float *sa, const void *B, con
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb, nullptr, M,
          2 * I, K, G, masked_m, 0, 0, 1, K / BK, nullptr, static_cast<uint8_t *>(Y), sy};
   return launch_tile<4, 2, 4, 4, 3, 4, MASKED, false, true>(a, G, static_cast<hipStream_t>(stream));
+}
+
+// BF16 GEMM without scales: shared checks (sizes in elements; bytes are twice)
+static int check_bf16(const void *A, const void *B, const void *D, int M, int N, int K,
+                      long long a_elems, long long b_elems, long long d_elems) {
+  if (M < 0 || N < 0 || K < 0) return FP8GEMM_INVALID_ARG;
+  if (M == 0 || N == 0) return -1;  // empty: nothing to do, success
+  if (!D) return FP8GEMM_INVALID_ARG;
+  if (K > 0 && (!A || !B)) return FP8GEMM_INVALID_ARG;
+  if (K % 64 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
+  const long long lim = 1LL << 30;  // 2^31 bytes
+  if (a_elems >= lim || b_elems >= lim || d_elems >= lim) return FP8GEMM_UNSUPPORTED_SHAPE;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16)) return FP8GEMM_MISALIGNED;
+  return FP8GEMM_OK;
+}
+
+int gemm_bf16_nt(const void *A, const void *B, void *D, int M, int N, int K, void *stream) {
+  const int st = check_bf16(A, B, D, M, N, K, (long long)M * K, (long long)N * K,
+                            (long long)M * N);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  Args a{static_cast<const uint8_t *>(A), nullptr, static_cast<const uint8_t *>(B), nullptr,
+         static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, 2 * K / BK, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= 128) return run_decode<true>(a, s);
+  return launch_tile<2, 4, 4, 4, 3, 4, DENSE, false, false, true>(a, 1, s);
+}
+
+int grouped_contiguous_bf16(const void *A, const void *B, void *D, int M, int N, int K, int G,
+                            void *stream, const int32_t *m_indices) {
+  if (G < 1) return FP8GEMM_INVALID_ARG;
+  const int st = check_bf16(A, B, D, M, N, K, (long long)M * K, (long long)G * N * K,
+                            (long long)M * N);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  if (!m_indices) return FP8GEMM_INVALID_ARG;
+  if (!aligned(m_indices, 4)) return FP8GEMM_MISALIGNED;
+  if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
+  Args a{static_cast<const uint8_t *>(A), nullptr, static_cast<const uint8_t *>(B), nullptr,
+         static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0, 1, 2 * K / BK, nullptr};
+  return launch_tile<4, 2, 4, 4, 3, 4, CONTIG, false, false, true>(
+      a, 1, static_cast<hipStream_t>(stream));
+}
+
+int grouped_masked_bf16(const void *A, const void *B, void *D, int M, int N, int K, int G,
+                        void *stream, const int32_t *masked_m, int expected_m) {
+  if (G < 1 || expected_m < 0) return FP8GEMM_INVALID_ARG;
+  const int st = check_bf16(A, B, D, M, N, K, (long long)G * M * K, (long long)G * N * K,
+                            (long long)G * M * N);
+  if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  if (!masked_m) return FP8GEMM_INVALID_ARG;
+  if (!aligned(masked_m, 4)) return FP8GEMM_MISALIGNED;
+  if (G > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
+  Args a{static_cast<const uint8_t *>(A), nullptr, static_cast<const uint8_t *>(B), nullptr,
+         static_cast<uint16_t *>(D), M, N, K, G, masked_m, 0, 0, 1, 2 * K / BK, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (expected_m <= 64)
+    return launch_tile<1, 4, 8, 1, 4, 4, MASKED, false, false, true>(a, G, s);
+  return launch_tile<1, 4, 8, 2, 4, 4, MASKED, false, false, true>(a, G, s);
 }
 
 const char *fp8gemm_status_string(int status) {

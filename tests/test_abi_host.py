@@ -23,6 +23,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"gemm_fp8_1x128_128x128_bf16", "grouped_contiguous",
                           "grouped_masked", "quantize_fp8_1x128",
                           "grouped_contiguous_swiglu_fp8", "grouped_masked_swiglu_fp8",
+                          "gemm_bf16_nt", "grouped_contiguous_bf16", "grouped_masked_bf16",
                           "fp8gemm_status_string"}
     for n in names:
         assert hasattr(lib, n), n
@@ -117,6 +118,38 @@ def test_swiglu_validation(lib):
     assert masked(mm=NUL) == INVALID
     assert masked(expected=-1) == INVALID
     assert masked(G=1 << 16, M=1, K=128) == SHAPE
+
+
+def test_bf16_validation(lib):
+    def dense(A=P, B=P, D=P, M=64, N=64, K=128):
+        return lib.gemm_bf16_nt(A, B, D, M, N, K, NUL)
+
+    def contig(G=2, M=256, K=128, idx=P, A=P):
+        return lib.grouped_contiguous_bf16(A, P, P, M, 64, K, G, NUL, idx)
+
+    def masked(G=4, M=256, K=128, mm=P, expected=64, D=P):
+        return lib.grouped_masked_bf16(P, P, D, M, 64, K, G, NUL, mm, expected)
+    assert dense(M=-1) == INVALID
+    assert dense(A=NUL) == INVALID
+    assert dense(D=NUL) == INVALID
+    assert dense(K=96) == SHAPE        # K must be a multiple of 64
+    assert dense(A=P_ODD) == MISALIGNED
+    assert dense(D=P_ODD) == MISALIGNED
+    assert dense(M=1 << 16, K=1 << 14) == SHAPE  # A past 2^31 bytes
+    assert dense(A=NUL, B=NUL, D=NUL, M=0) == OK
+    assert dense(A=NUL, B=NUL, D=NUL, N=0) == OK
+    assert contig(G=0) == INVALID
+    assert contig(idx=NUL) == INVALID
+    assert contig(M=200) == SHAPE
+    assert contig(K=32) == SHAPE
+    assert contig(idx=ctypes.c_void_p(0x10001)) == MISALIGNED
+    assert contig(A=P_ODD) == MISALIGNED
+    assert masked(G=0) == INVALID
+    assert masked(expected=-1) == INVALID
+    assert masked(mm=NUL) == INVALID
+    assert masked(K=100) == SHAPE
+    assert masked(D=P_ODD) == MISALIGNED
+    assert masked(G=1 << 16, M=1, K=64) == SHAPE
 
 
 def test_binding_rejects_bad_tensors():
