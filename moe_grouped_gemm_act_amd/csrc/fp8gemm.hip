@@ -575,8 +575,14 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         const float sbv = s_sb[hsb][t];
         v8i bfr[TN], afr[2];
         float scb[TM];
+        // Large tiles (WGN > 1): only the first two weight fragments are read
+        // before the first MFMA and the rest one MFMA ahead of use, so the
+        // eight compute waves, released together by the barrier, do not all
+        // queue their whole fragment reads on the LDS at once (measured 1-2%
+        // on the prefill and contiguous shapes, nothing on the narrow tiles)
+        constexpr int B0 = WGN > 1 && TN > 2 ? 2 : TN;
 #pragma unroll
-        for (int i = 0; i < TN; ++i) {
+        for (int i = 0; i < B0; ++i) {
           const int row = BM + (wn * TN + i) * 16 + fr;
           bfr[i] = frag(sl + row * BK, row, fg);
         }
@@ -594,6 +600,11 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
           }
 #pragma unroll
           for (int i = 0; i < TN; ++i) {
+            if (j == 0 && i + B0 < TN) {
+              asm volatile("" ::: "memory");  // keeps the read after the MFMAs before it
+              const int row = BM + (wn * TN + i + B0) * 16 + fr;
+              bfr[i + B0] = frag(sl + row * BK, row, fg);
+            }
             const int k = j * TN + i;
             ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
