@@ -1,0 +1,96 @@
+"""HIP-graph capture of every entry point beyond the dense GEMM (whose
+split-K replay is tested with the parity cases): each graph is replayed
+several times, with the output cleared and eager launches of the same call
+in between, and every replay must equal the eager result bit for bit (all
+kernels are deterministic: no atomics, fixed summation order)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_act_amd as fg
+import synth
+from synth import workloads as W
+from parity_util import to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def replay_equals_eager(what, call, outs):
+    """call() launches on the current stream into `outs`; returns after
+    checking three replays of its captured graph against the eager result."""
+    s = torch.cuda.Stream()
+    for o in outs:
+        o.zero_()  # rows a call does not write (padding, masked) must compare equal too
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        call()  # eager first: any per-stream workspace is made outside capture
+    s.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for r in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), f"{what}: replay {r} differs"
+        with torch.cuda.stream(s):
+            call()  # eager work between replays
+        s.synchronize()
+    announce(f"{what}: 3 replays equal the eager result")
+
+
+def test_graph_quantize():
+    M, K = 300, 1024
+    x = synth.normal(8800, M * K).reshape(M, K)
+    X = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    A = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
+    replay_equals_eager("quantize 300x1024", lambda: fg.quantize_fp8_1x128(X, A, sa), [A, sa])
+
+
+def test_graph_masked_fp8():
+    d = W.masked(8810, 4, 192, 512, 1024)
+    A, sa, B, sb = (to_gpu(d[k]) for k in ("A", "sa", "B", "sb"))
+    mm = to_gpu(d["masked_m"])
+    D = torch.empty((4, 192, 512), dtype=torch.bfloat16, device="cuda")
+    replay_equals_eager("masked 4x192x512x1024",
+                        lambda: fg.grouped_masked(A, sa, B, sb, mm, 96, D), [D])
+
+
+def test_graph_swiglu_contiguous_and_masked():
+    G, rows, I, K = 3, 768, 256, 1024
+    idx, _ = synth.contiguous_indices(8823, G, rows, False)
+    A, sa = synth.act(8820, rows, K)
+    B, sb = synth.grouped_weight(8821, G, 2 * I, K)
+    tA, tsa, tB, tsb, tidx = to_gpu(A), to_gpu(sa), to_gpu(B), to_gpu(sb), to_gpu(idx)
+    Y = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    sy = torch.empty((I // 128, rows), dtype=torch.float32, device="cuda")
+    replay_equals_eager("contiguous swiglu 768x512x1024",
+                        lambda: fg.grouped_contiguous_swiglu_fp8(tA, tsa, tB, tsb, tidx, Y, sy), [Y, sy])
+    Am, sam = synth.grouped_act(8830, G, 192, K)
+    mm = to_gpu(np.array([192, 5, 0], np.int32))
+    tAm, tsam = to_gpu(Am), to_gpu(sam)
+    Ym = torch.empty((G, 192, I), dtype=torch.uint8, device="cuda")
+    sym = torch.empty((G, I // 128, 192), dtype=torch.float32, device="cuda")
+    replay_equals_eager("masked swiglu 3x192x512x1024",
+                        lambda: fg.grouped_masked_swiglu_fp8(tAm, tsam, tB, tsb, mm, 64, Ym, sym), [Ym, sym])
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 2112, 7168), (300, 520, 640)])
+def test_graph_bf16_dense(M, N, K):
+    """the first shape takes the split-K decode path (workspace + reduction)"""
+    a = torch.from_numpy(synth.normal(8840, M * K).reshape(M, K)).to(torch.bfloat16).cuda()
+    b = torch.from_numpy(synth.normal(8841, N * K).reshape(N, K)).to(torch.bfloat16).cuda()
+    D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    replay_equals_eager(f"bf16 {M}x{N}x{K}", lambda: fg.gemm_bf16_nt(a, b, D), [D])

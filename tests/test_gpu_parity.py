@@ -194,8 +194,9 @@ def test_decode_variants_full(M, N, K, monkeypatch):
 
 
 def test_decode_graph_replay():
-    """Captured split-K launches: every replay equals the eager result (the
-    arrival counters are re-armed by the kernel, no memset in the graph)."""
+    """Captured split-K launches (partial products, then their reduction):
+    every replay equals the eager result; the stream's workspace is made by
+    the eager call before capture and nothing in the graph is a memset."""
     M, N, K = 128, 2112, 7168
     d = W.dense(1600, M, N, K)
     A, sa, B, sb = to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"])
