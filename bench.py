@@ -341,6 +341,7 @@ def profile_commands(workload, out="gpurun_out/prof"):
         ("kt", f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/{w}/kt -o {w} -- {b} --steps 20 --warmup 5"),
         ("fetch", f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/{w}/fetch -o {w} -- {b} --steps 2 --warmup 1"),
         ("write", f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/{w}/write -o {w} -- {b} --steps 2 --warmup 1"),
+        ("sq", f"rocprofv3 --pmc SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT --output-format csv -d {out}/{w}/sq -o {w} -- {b} --steps 2 --warmup 1"),
         ("cfetch", f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/copy/fetch -o copy -- python3 bench.py --copy-probe 1024"),
         ("cwrite", f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/copy/write -o copy -- python3 bench.py --copy-probe 1024"),
     ]
@@ -421,9 +422,36 @@ def summarize_profile(d, workload):
         kib = st.mean(float(r["Counter_Value"]) for r in rs)
         return (1 << 30) / (kib * 1024), kib
 
+    def sq_counters():
+        """per call: mean over launches of each SQ counter (summed over the
+        launch's kernels), from the multi-counter pass; None if not taken"""
+        if not glob.glob(os.path.join(d, w, "sq", "*counter_collection.csv")):
+            return None
+        by_disp = {}
+        for r in rows(f"{w}/sq/*counter_collection.csv"):
+            if _ours(r["Kernel_Name"]):
+                e = by_disp.setdefault(int(r["Dispatch_Id"]), {"Kernel_Name": r["Kernel_Name"]})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        grps = _launches([by_disp[k] for k in sorted(by_disp)])
+        cc = _call_of_dispatches(len(grps), _last_json(os.path.join(d, w, "sq.log")))
+        out = {}
+        for grp, c in zip(grps, cc):
+            tot = {}
+            for e in grp:
+                for k, v in e.items():
+                    if k != "Kernel_Name":
+                        tot[k] = tot.get(k, 0.0) + v
+            out.setdefault(c, []).append(tot)
+        return {c: {k: st.mean(t[k] for t in v) for k in v[0]} for c, v in out.items()}
+
     fscale, fkib = copy_scale("fetch", "FETCH_SIZE")
     wscale, wkib = copy_scale("write", "WRITE_SIZE")
     fetch, write = counter("fetch"), counter("write")
+    sq = sq_counters()
+    sq_table = []
+    if sq:
+        agent = [r for r in rows(f"{w}/sq/*agent_info.csv") if int(r.get("Simd_Count") or 0) > 0][0]
+        n_simd, n_arr = int(agent["Simd_Count"]), int(agent["Array_Count"])
     table, traffic = [], {}
     import re
     for i, lab in enumerate(labels):
@@ -441,6 +469,12 @@ def summarize_profile(d, workload):
         wb = st.mean(write[i]) * wscale
         alg = kline["per_call"][i]["bytes"]
         traffic[lab] = {"fetch_bytes": fb, "write_bytes": wb}
+        if sq and i in sq:
+            q = sq[i]
+            busy = q["SQ_BUSY_CYCLES"] / n_arr  # per shader array: the launch's cycles
+            sq_table.append(f"| {lab} | {q['SQ_VALU_MFMA_BUSY_CYCLES'] / n_simd / busy:.3f} | "
+                            f"{q['SQ_LDS_BANK_CONFLICT'] / max(q['SQ_LDS_IDX_ACTIVE'], 1):.3f} | "
+                            f"{busy / (st.mean(durs) * 1e3):.2f} |")
         table.append(f"| {lab} | `{name}` | {grid[0]},{grid[1]} | {len(durs)} | {st.mean(durs):.2f} | "
                      f"{st.median(durs):.2f} | {min(durs):.2f} | {kline['per_call'][i]['avg_us']:.2f} | "
                      f"{fb / 1e6:.2f} | {wb / 1e6:.2f} | {alg / 1e6:.2f} | {(fb + wb) / alg:.2f} |")
@@ -471,6 +505,16 @@ algorithmic bytes (A, B, scales and D once each).
 Calibration: a 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE {fkib:.0f} KiB and
 WRITE_SIZE {wkib:.0f} KiB per dispatch: scale factors {fscale:.3f} (fetch) and {wscale:.3f} (write).
 """
+    if sq_table:
+        md += f"""
+SQ counters (the `sq` pass, means over launches).  "MFMA busy" =
+SQ_VALU_MFMA_BUSY_CYCLES / {n_simd} SIMDs over SQ_BUSY_CYCLES / {n_arr} shader arrays (the
+launch's own cycles); "LDS conflicts" = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; "GHz" = those
+busy cycles over the traced mean duration (the clock the launch ran at, approximately).
+
+| call | MFMA busy | LDS conflicts | GHz |
+|---|---|---|---|
+""" + "\n".join(sq_table) + "\n"
     open(os.path.join(ROOT, "profiles", f"{w}.md"), "w").write(md)
     json.dump({"source_sha256": sha, "fetch_scale": fscale, "write_scale": wscale, "kernels": traffic},
               open(os.path.join(ROOT, "profiles", f"{w}.traffic.json"), "w"), indent=1)
