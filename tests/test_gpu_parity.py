@@ -397,3 +397,32 @@ def test_masked_workload_sampled(case):
     pn = np.concatenate([pn, rng.integers(0, N, 2 * len(gs))])
     ref = oracle.points("masked", d["A"], d["sa"], d["B"], d["sb"], pm, pn, pg=pg)
     assert_close(out[pg, pm, pn], ref, f"masked G={G} N={N} K={K}")
+
+
+# ------------------------------------------------- K past the tile kernel ----
+
+
+def test_long_k_fallback_all_layouts():
+    """K = 20608 (161 blocks) is past the tile kernel's weight-scale preload:
+    the register-staged fallback kernel serves all three layouts."""
+    K = 20608
+    announce(f"long-K fallback dense 200x300x{K}")
+    d = W.dense(1900, 200, 300, K)
+    assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), "long K dense")
+    announce(f"long-K fallback contiguous G=2 256x200x{K}")
+    c = W.contiguous(1910, 2, 256, 200, K, uniform=False)
+    out = gpu_contig(c)
+    ref = oracle.grouped_contiguous(c["A"], c["sa"], c["B"], c["sb"], c["m_indices"],
+                                    np.full((c["M"], c["N"]), SENTINEL, np.uint16))
+    pad = c["m_indices"] < 0
+    assert (out[pad] == SENTINEL).all() and (out[~pad] != SENTINEL).all()
+    assert_close(out[~pad], ref[~pad], "long K contiguous")
+    announce(f"long-K fallback masked G=2 100x130x{K}")
+    m = W.masked(1920, 2, 100, 130, K)
+    m["masked_m"] = np.array([100, 37], np.int32)
+    out = gpu_masked(m)
+    ref = oracle.grouped_masked(m["A"], m["sa"], m["B"], m["sb"], m["masked_m"],
+                                np.full((2, 100, 130), SENTINEL, np.uint16))
+    live = np.arange(100)[None, :] < m["masked_m"][:, None]
+    assert (out[~live] == SENTINEL).all()
+    assert_close(out[live], ref[live], "long K masked")
