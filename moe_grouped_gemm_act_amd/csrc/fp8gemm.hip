@@ -950,12 +950,13 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= 128 && K <= 20480) return run_decode<false>(a, s);
   if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
-  // 256 activation rows x 128 weight rows, eight compute waves (two per
+  // 256 weight rows x 128 activation rows, eight compute waves (two per
   // SIMD, so one wave's promotion FMAs run under the other's MFMAs) and four
-  // loader waves; FP8GEMM_LARGE=6 selects the four-compute-wave layout
+  // loader waves (measured 1.5-2% faster on the prefill shapes than 128 x
+  // 256 tiles); FP8GEMM_LARGE=6 selects the four-compute-wave layout
   const char *e = getenv("FP8GEMM_LARGE");
   if (e && e[0] == '6') return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
-  return launch_tile<2, 4, 4, 4, 3, 4, DENSE>(a, 1, s);
+  return launch_tile<4, 2, 4, 4, 3, 4, DENSE>(a, 1, s);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
