@@ -94,3 +94,57 @@ def test_graph_bf16_dense(M, N, K):
     b = torch.from_numpy(synth.normal(8841, N * K).reshape(N, K)).to(torch.bfloat16).cuda()
     D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     replay_equals_eager(f"bf16 {M}x{N}x{K}", lambda: fg.gemm_bf16_nt(a, b, D), [D])
+
+
+def test_capture_before_any_workspace_runs_unsplit():
+    """A split-K shape captured on a stream that has never run an eager call
+    has no workspace yet: the captured launch runs without a K split (no
+    allocation during capture) and still matches the oracle."""
+    import oracle
+    from parity_util import assert_close, bits, sentinel_out
+    M, N, K = 64, 2112, 7168
+    d = W.dense(8850, M, N, K)
+    A, sa, B, sb = (to_gpu(d[k]) for k in ("A", "sa", "B", "sb"))
+    s = torch.cuda.Stream()
+    D = sentinel_out((M, N))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
+    with torch.cuda.stream(s):
+        g.replay()
+    s.synchronize()
+    rng = np.random.default_rng(8850)
+    pm, pn = rng.integers(0, M, 3000), rng.integers(0, N, 3000)
+    got = bits(D)
+    assert_close(got[pm, pn], oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn),
+                 "captured without a workspace")
+    announce("capture before any workspace: matches the oracle")
+
+
+def test_two_streams_split_k_concurrently():
+    """Split-K calls on two streams at once use separate workspaces: both
+    results equal the same calls made one after the other."""
+    from parity_util import bits, sentinel_out
+    shapes = [(64, 2112, 7168, 8860), (128, 4096, 7168, 8861)]
+    ins = []
+    for M, N, K, seed in shapes:
+        d = W.dense(seed, M, N, K)
+        ins.append(((to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"])), (M, N)))
+    ref = []
+    for (A, sa, B, sb), (M, N) in ins:
+        D = sentinel_out((M, N))
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
+        torch.cuda.synchronize()
+        ref.append(bits(D))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [sentinel_out(mn) for _, mn in ins]
+    torch.cuda.synchronize()
+    for _ in range(5):  # interleave launches on the two streams
+        for (args, _), s, D in zip(ins, streams, outs):
+            with torch.cuda.stream(s):
+                fg.gemm_fp8_1x128_128x128_bf16(*args, D)
+    torch.cuda.synchronize()
+    for D, r in zip(outs, ref):
+        assert (bits(D) == r).all()
+    announce("two streams: split-K results equal the serial ones")
