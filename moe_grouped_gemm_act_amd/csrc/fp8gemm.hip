@@ -71,6 +71,10 @@ struct Args {
   float *ws;                 // split-K partial planes [splits][M][N] (splits > 1)
   uint8_t *act;              // fused SwiGLU: e4m3 codes of y [M][N/2] (masked [G][M][N/2]) ...
   float *act_scale;          // ... and their 1x128 scales [N/256][M] ([G][N/256][M])
+  // tail split (dense, large M): tiles past full_tiles are split over K into
+  // tail_splits items of tail_kb blocks each, whose fp32 partials go to ws
+  // tile by tile and are summed by tail_reduce_kernel
+  int full_tiles, tail_splits, tail_kb;
 };
 
 // XOR key of an LDS row: 16-byte chunk c of row r sits at position
@@ -366,12 +370,23 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   // XCD share panels
   constexpr int GROUPN = 4;
   const int T = a.tiles_m * a.tiles_n, S = KSPLIT ? a.splits : 1;
-  int item = blockIdx.x;
-  {
-    const int TS = T * S, x = item % 8, l = item / 8, per = TS / 8, rem = TS % 8;
+  // Tail split: when the last wave of tiles would leave most CUs idle, the
+  // tiles past full_tiles are split over K.  Their items take the highest
+  // workgroup ids, which are dispatched last, once CUs free up, round robin
+  // over the XCDs; the full tiles keep the XCD-aware order below.
+  const bool tail = !KSPLIT && LAYOUT == DENSE && a.tail_splits > 1 && (int)blockIdx.x >= a.full_tiles;
+  int item = blockIdx.x, split, tile;
+  if (tail) {
+    const int r = item - a.full_tiles;
+    tile = a.full_tiles + r / a.tail_splits;
+    split = r % a.tail_splits;
+  } else {
+    const int TS = (!KSPLIT && a.tail_splits > 1) ? a.full_tiles : T * S;
+    const int x = item % 8, l = item / 8, per = TS / 8, rem = TS % 8;
     item = x * per + min(x, rem) + l;
+    split = item / T;
+    tile = item % T;
   }
-  const int split = item / T, tile = item % T;
   int tn, tm;
   {
     const int gsz = GROUPN * a.tiles_m, grp = tile / gsz, in = tile % gsz;
@@ -380,7 +395,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     tm = in / gw;
   }
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kb0 = split * a.kb_per_split, nk = max(0, min(Kb - kb0, a.kb_per_split));
+  const int kbps = tail ? a.tail_kb : a.kb_per_split;
+  const int kb0 = split * kbps, nk = max(0, min(Kb - kb0, kbps));
 
   const uint8_t *A = a.A, *B = a.B;
   const float *sa = a.sa, *sb = a.sb;
@@ -695,6 +711,18 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     return;
   }
 
+  if (tail) {
+    // this K part of a tail tile: its fp32 partial tile goes to workspace
+    // slot (tail tile, split), BM x BN floats, row-major within the tile
+    float *pt = a.ws + ((size_t)(tile - a.full_tiles) * a.tail_splits + split) * (BM * BN);
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        *reinterpret_cast<v4f *>(pt + ((wm * TM + j) * 16 + fr) * BN + (wn * TN + i) * 16 + 4 * fg) =
+            acc[i][j];
+    return;
+  }
   if (S > 1) {
     // this split's fp32 partial goes to its own [M][N] plane of the
     // workspace; splitk_reduce_kernel (next on the stream) sums the planes
@@ -785,6 +813,39 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, uin
     *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
   } else {
     if (n < N) dp[0] = (uint16_t)b0;
+    if (n + 1 < N) dp[1] = (uint16_t)b1;
+    if (n + 2 < N) dp[2] = (uint16_t)b2;
+    if (n + 3 < N) dp[3] = (uint16_t)b3;
+  }
+}
+
+// Tail-split reduction: tail tile t (of R) has S partial tiles of BM x BN
+// floats in ws; D gets their sum in split order, rounded to bf16.  One
+// thread per 4 consecutive columns of a tile row; the tile's position comes
+// from the same GROUPN walk as the tile kernel's.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float *ws, uint16_t *D, int M, int N,
+                                                          int full_tiles, int S, int tiles_m,
+                                                          int tiles_n) {
+  constexpr int GROUPN = 4, QT = BM * BN / 4;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  const int t = q / QT, e = q % QT;  // tail tile, quad inside it (grid: whole tiles)
+  const int tile = full_tiles + t;
+  const int gsz = GROUPN * tiles_m, grp = tile / gsz, in = tile % gsz;
+  const int gw = min(GROUPN, tiles_n - grp * GROUPN);
+  const int ml = e / (BN / 4), nl = (e % (BN / 4)) * 4;
+  const int m = (in / gw) * BM + ml, n = (grp * GROUPN + in % gw) * BN + nl;
+  if (m >= M || n >= N) return;
+  const float *p = ws + (size_t)t * S * (BM * BN) + ml * BN + nl;
+  v4f sum = *reinterpret_cast<const v4f *>(p);
+  for (int s = 1; s < S; ++s) sum += *reinterpret_cast<const v4f *>(p + (size_t)s * (BM * BN));
+  uint16_t *dp = D + (size_t)m * N + n;
+  const uint32_t b0 = bf16_bits(sum[0]), b1 = bf16_bits(sum[1]), b2 = bf16_bits(sum[2]),
+                 b3 = bf16_bits(sum[3]);
+  if ((N & 3) == 0 && n + 3 < N) {
+    *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+  } else {
+    dp[0] = (uint16_t)b0;
     if (n + 1 < N) dp[1] = (uint16_t)b1;
     if (n + 2 < N) dp[2] = (uint16_t)b2;
     if (n + 3 < N) dp[3] = (uint16_t)b3;
@@ -919,6 +980,39 @@ int launch(Args a, int groups, hipStream_t stream) {
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
+// Dense M > 128 with 256 x 128 tiles.  When the tiles leave a last wave of
+// R <= 128 tiles for the 256 CUs, those R tiles are split over K into
+// S = min(8, 256 / R) parts (each at least 4 K blocks) that run as the last
+// items of the same grid, and tail_reduce_kernel adds the parts.  Without a
+// workspace (first call on a stream under capture) the tail is not split.
+int launch_dense_large(Args a, hipStream_t stream) {
+  constexpr int BN = 256, BM = 128;
+  const int tiles_m = cdiv(a.M, BM), tiles_n = cdiv(a.N, BN), T = tiles_m * tiles_n;
+  const int Kb = a.K / BK, R = T % 256;
+  int S = R > 0 && R <= 128 ? std::min(8, 256 / R) : 1;
+  while (S > 1 && cdiv(Kb, S) < 4) --S;
+  const Workspace *w = S > 1 ? workspace(stream) : nullptr;
+  if (S > 1 && (!w || (size_t)R * S * BM * BN > WS_FLOATS)) S = 1;
+  if (S <= 1) return launch_tile<4, 2, 4, 4, 3, 4, DENSE>(a, 1, stream);
+  const int kb = cdiv(Kb, S);
+  a.tiles_m = tiles_m;
+  a.tiles_n = tiles_n;
+  a.splits = 1;
+  a.kb_per_split = Kb;
+  a.full_tiles = T - R;
+  a.tail_splits = cdiv(Kb, kb);
+  a.tail_kb = kb;
+  a.ws = w->part;
+  void *kargs[] = {&a};
+  hipError_t er = hipLaunchKernel(
+      reinterpret_cast<const void *>(&tile_kernel<4, 2, 4, 4, 3, 4, false, false, DENSE, false>),
+      dim3(a.full_tiles + R * a.tail_splits), dim3((8 + 4) * 64), kargs, 0, stream);
+  if (er != hipSuccess) return FP8GEMM_LAUNCH_FAILED;
+  hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(R * (BM * BN / 4) / 256), dim3(256), 0, stream,
+                     a.ws, a.D, a.M, a.N, a.full_tiles, a.tail_splits, tiles_m, tiles_n);
+  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+}
+
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Checks shared by the three calls.  Runs before any HIP call.
@@ -956,7 +1050,7 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   // 256 tiles); FP8GEMM_LARGE=6 selects the four-compute-wave layout
   const char *e = getenv("FP8GEMM_LARGE");
   if (e && e[0] == '6') return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
-  return launch_tile<4, 2, 4, 4, 3, 4, DENSE>(a, 1, s);
+  return launch_dense_large(a, s);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,

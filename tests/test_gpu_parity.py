@@ -244,6 +244,34 @@ def test_prefill_workload_sampled(M, N, K):
     assert_close(out[pm, pn], ref, f"prefill {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(384, 1300, 3200), (300, 520, 2048), (700, 600, 4096)])
+def test_dense_tail_split_full(M, N, K):
+    """Fewer than half a wave of 256 x 128 tiles: every tile is split over K
+    (up to eight parts, the last one shorter) and the parts are summed by the
+    tail reduction."""
+    seed = 3500 + M + N
+    announce(f"tail split dense {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K)
+    assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), f"tail {M}x{N}x{K}")
+
+
+def test_dense_tail_split_sampled():
+    """270 tiles of 256 x 128: 256 run whole, the last 14 (rows 1664..2303,
+    columns 3072..3839 in the tile walk) are split in two over K."""
+    M, N, K = 2304, 3840, 1024
+    seed = 3600
+    announce(f"tail split dense {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K)
+    out = gpu_dense(d)
+    assert (out != SENTINEL).all()
+    rng = np.random.default_rng(seed)
+    pm, pn = sample_points(rng, M, N, 3000)
+    pm = np.concatenate([pm, rng.integers(1664, M, 3000), np.arange(1664, M)])
+    pn = np.concatenate([pn, rng.integers(3072, N, 3000), np.full(M - 1664, N - 1)])
+    ref = oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn)
+    assert_close(out[pm, pn], ref, f"tail {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------- contiguous ---
 
 
