@@ -980,20 +980,21 @@ int launch(Args a, int groups, hipStream_t stream) {
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
-// Dense M > 128 with 256 x 128 tiles.  When the tiles leave a last wave of
-// R <= 128 tiles for the 256 CUs, those R tiles are split over K into
+// Dense M > 128 with one large tile per CU.  When the tiles leave a last
+// wave of R <= 128 tiles for the 256 CUs, those R tiles are split over K into
 // S = min(8, 256 / R) parts (each at least 4 K blocks) that run as the last
 // items of the same grid, and tail_reduce_kernel adds the parts.  Without a
 // workspace (first call on a stream under capture) the tail is not split.
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool BF = false>
 int launch_dense_large(Args a, hipStream_t stream) {
-  constexpr int BN = 256, BM = 128;
+  constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   const int tiles_m = cdiv(a.M, BM), tiles_n = cdiv(a.N, BN), T = tiles_m * tiles_n;
-  const int Kb = a.K / BK, R = T % 256;
+  const int Kb = (BF ? 2 * a.K : a.K) / BK, R = T % 256;
   int S = R > 0 && R <= 128 ? std::min(8, 256 / R) : 1;
   while (S > 1 && cdiv(Kb, S) < 4) --S;
   const Workspace *w = S > 1 ? workspace(stream) : nullptr;
   if (S > 1 && (!w || (size_t)R * S * BM * BN > WS_FLOATS)) S = 1;
-  if (S <= 1) return launch_tile<4, 2, 4, 4, 3, 4, DENSE>(a, 1, stream);
+  if (S <= 1) return launch_tile<WGN, WGM, TN, TM, STAGES, NLD, DENSE, false, false, BF>(a, 1, stream);
   const int kb = cdiv(Kb, S);
   a.tiles_m = tiles_m;
   a.tiles_n = tiles_n;
@@ -1005,8 +1006,9 @@ int launch_dense_large(Args a, hipStream_t stream) {
   a.ws = w->part;
   void *kargs[] = {&a};
   hipError_t er = hipLaunchKernel(
-      reinterpret_cast<const void *>(&tile_kernel<4, 2, 4, 4, 3, 4, false, false, DENSE, false>),
-      dim3(a.full_tiles + R * a.tail_splits), dim3((8 + 4) * 64), kargs, 0, stream);
+      reinterpret_cast<const void *>(
+          &tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, false, false, DENSE, BF>),
+      dim3(a.full_tiles + R * a.tail_splits), dim3((WGN * WGM + NLD) * 64), kargs, 0, stream);
   if (er != hipSuccess) return FP8GEMM_LAUNCH_FAILED;
   hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(R * (BM * BN / 4) / 256), dim3(256), 0, stream,
                      a.ws, a.D, a.M, a.N, a.full_tiles, a.tail_splits, tiles_m, tiles_n);
@@ -1050,7 +1052,7 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   // 256 tiles); FP8GEMM_LARGE=6 selects the four-compute-wave layout
   const char *e = getenv("FP8GEMM_LARGE");
   if (e && e[0] == '6') return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
-  return launch_dense_large(a, s);
+  return launch_dense_large<4, 2, 4, 4, 3, 4>(a, s);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -1159,7 +1161,7 @@ int gemm_bf16_nt(const void *A, const void *B, void *D, int M, int N, int K, voi
          static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, 2 * K / BK, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= 128) return run_decode<true>(a, s);
-  return launch_tile<2, 4, 4, 4, 3, 4, DENSE, false, false, true>(a, 1, s);
+  return launch_dense_large<2, 4, 4, 4, 3, 4, true>(a, s);
 }
 
 int grouped_contiguous_bf16(const void *A, const void *B, void *D, int M, int N, int K, int G,
