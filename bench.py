@@ -348,7 +348,7 @@ def profile_commands(workload, out="gpurun_out/prof"):
 
 
 _PRIMARY = ("tile_kernel", "gemm_kernel", "quant_kernel")
-_FOLLOWER = ("splitk_reduce_kernel",)  # runs right after its call's tile kernel
+_FOLLOWER = ("splitk_reduce_kernel", "tail_reduce_kernel")  # run right after their call's tile kernel
 
 
 def _ours(name):
@@ -461,7 +461,7 @@ def summarize_profile(d, workload):
         r0 = grps[0][0]
         names = []
         for r in grps[0]:
-            m = re.search(r"(tile_kernel|gemm_kernel)<[^>]*>|splitk_reduce_kernel|quant_kernel", r["Kernel_Name"])
+            m = re.search(r"(tile_kernel|gemm_kernel|tail_reduce_kernel)<[^>]*>|splitk_reduce_kernel|quant_kernel", r["Kernel_Name"])
             names.append(m.group(0) if m else r["Kernel_Name"])
         name = " + ".join(names)
         grid = (int(r0["Grid_Size_X"]) // int(r0["Workgroup_Size_X"]), int(r0["Grid_Size_Y"]))
@@ -492,7 +492,7 @@ Commands (repository root, one MI355X, after `cd /tmp && export TMPDIR=/tmp`), t
 {cmds}
 
 Per call: kernel trace durations (all launches of that call in the traced bench run; a
-split-K call's launch is its tile kernel plus the reduction kernel, durations added), the
+split-K or tail-split call's launch is its tile kernel plus the reduction kernel, durations added), the
 bench's own HIP-event average for the same call in that run (launch gaps included, and
 stretched by the tracer), and HBM bytes per launch from the two counter runs, scaled by the
 copy calibration below; grid is the first kernel's.  "ratio" = measured HBM bytes /
