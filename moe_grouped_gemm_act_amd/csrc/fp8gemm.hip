@@ -35,6 +35,7 @@
 // device-side row count and tiles past it exit before loading anything.
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <stdint.h>
 
 #include <algorithm>
@@ -331,6 +332,158 @@ __device__ __forceinline__ int fresh_lane_id() {
   return l;
 }
 
+// Pieces of a compute wave's work shared by the tile kernel and the
+// persistent walk below.  A compute wave (wn, wm) of a WGN-wide grid owns
+// weight rows (wn TN + i) 16 + 0..15 and activation rows (wm TM + j) 16 +
+// 0..15 of the block tile; slot rows 0..BM-1 are activations, BM.. weights.
+
+// Product k = j * TN + i of a K block (activation group j, weight group i)
+// comes from one MFMA; it is promoted LAG MFMAs later, when it has long
+// landed, so the promotion FMAs issue in the shadow of the next MFMAs instead
+// of waiting on the one just issued.  Products sit in a ring of RING
+// registers; TN * TM is a multiple of RING, so slots and the promotion of the
+// previous block's last products line up across blocks.
+constexpr int LAG = 2, RING = 4;
+
+// One FP8 K block from slot `sl` (activation scales after the operand rows),
+// with the wave's weight scale sbv: acc += (sa sb) (A_blk B_blk^T), the last
+// LAG products carried to the next block (or fp8_flush).  The next activation
+// fragment and its scale are read from LDS one group ahead.  Large tiles
+// (WGN > 1) read only their first two weight fragments before the first MFMA
+// and the rest one MFMA ahead of use, so the compute waves, released together
+// by the barrier, do not all queue their whole fragment reads on the LDS at
+// once.
+template <int WGN, int TN, int TM, int BM>
+__device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn, int wm, int fr,
+                                           int fg, v4f (&acc)[TN][TM], v4f (&ring)[RING],
+                                           float &sc_last) {
+  constexpr int ROWS = BM + WGN * TN * 16;
+  static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
+  const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
+  v8i bfr[TN], afr[2];
+  float scb[TM];
+  constexpr int B0 = WGN > 1 && TN > 2 ? 2 : TN;
+#pragma unroll
+  for (int i = 0; i < B0; ++i) {
+    const int row = BM + (wn * TN + i) * 16 + fr;
+    bfr[i] = frag(sl + row * BK, row, fg);
+  }
+  {
+    const int row = wm * TM * 16 + fr;
+    afr[0] = frag(sl + row * BK, row, fg);
+    scb[0] = ssl[row] * sbv;
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    if (j + 1 < TM) {
+      const int row = (wm * TM + j + 1) * 16 + fr;
+      afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
+      scb[j + 1] = ssl[row] * sbv;
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      if (j == 0 && i + B0 < TN) {
+        asm volatile("" ::: "memory");  // keeps the read after the MFMAs before it
+        const int row = BM + (wn * TN + i + B0) * 16 + fr;
+        bfr[i + B0] = frag(sl + row * BK, row, fg);
+      }
+      const int k = j * TN + i;
+      ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+      const int kp = k - LAG;                      // product promoted now
+      const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
+      const float sp = kp >= 0 ? scb[kq / TN] : sc_last;
+      v4f &ap = acc[kq % TN][kq / TN];
+      const v4f &pp = ring[(kq + RING) % RING];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ap[r] = __builtin_fmaf(pp[r], sp, ap[r]);
+    }
+  }
+  sc_last = scb[TM - 1];
+}
+
+// the last block's last LAG products
+template <int TN, int TM>
+__device__ __forceinline__ void fp8_flush(v4f (&acc)[TN][TM], const v4f (&ring)[RING], float sc_last) {
+#pragma unroll
+  for (int k = TN * TM - LAG; k < TN * TM; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
+}
+
+// One BF16 K block (64 elements, 128 bytes a row).  No scales, so products
+// accumulate straight in the MFMA's own accumulator.  A lane's two 16-byte
+// chunks of a block row hold elements 8g..8g+7 and 32+8g..32+8g+7 (g = lane
+// / 16): exactly the operands of two 16x16x32 bf16 MFMAs, over the block's
+// first and second 32 elements.  All sub-tiles take the first half before
+// the second, so no MFMA waits on the one just issued.
+template <int TN, int TM, int BM>
+__device__ __forceinline__ void bf16_kblock(const uint8_t *sl, int wn, int wm, int fr, int fg,
+                                            v4f (&acc)[TN][TM]) {
+  v8i bfr[TN], afr[TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int row = BM + (wn * TN + i) * 16 + fr;
+    bfr[i] = frag(sl + row * BK, row, fg);
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int row = (wm * TM + j) * 16 + fr;
+    afr[j] = frag(sl + row * BK, row, fg);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_half(bfr[i], h), bf_half(afr[j], h),
+                                                            acc[i][j], 0, 0, 0);
+}
+
+// The wave's part of a BM x BN fp32 tile, row-major, at pt (tail-split parts).
+template <int TN, int TM, int BN>
+__device__ __forceinline__ void store_part(const v4f (&acc)[TN][TM], float *pt, int wn, int wm,
+                                           int fr, int fg) {
+#pragma unroll
+  for (int j = 0; j < TM; ++j)
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      *reinterpret_cast<v4f *>(pt + ((wm * TM + j) * 16 + fr) * BN + (wn * TN + i) * 16 + 4 * fg) =
+          acc[i][j];
+}
+
+// The wave's part of the output tile at (m0, n0) as bf16: rows below mvalid
+// (CONTIG: rows whose index names expert g).
+template <int TN, int TM, int LAYOUT>
+__device__ __forceinline__ void store_bf16(const v4f (&acc)[TN][TM], uint16_t *D, const int32_t *idx,
+                                           int g, int M, int N, int mvalid, int m0, int n0, int wn,
+                                           int wm, int fr, int fg) {
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + (wm * TM + j) * 16 + fr;
+    bool ok = m < mvalid;
+    if (LAYOUT == CONTIG) ok = m < M && idx[m] == g;
+    if (!ok) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int n = n0 + (wn * TN + i) * 16 + 4 * fg;
+      uint16_t *dp = D + (size_t)m * N + n;
+      const uint32_t b0 = bf16_bits(acc[i][j][0]), b1 = bf16_bits(acc[i][j][1]);
+      const uint32_t b2 = bf16_bits(acc[i][j][2]), b3 = bf16_bits(acc[i][j][3]);
+      if ((N & 3) == 0 && n + 3 < N) {
+        *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+      } else {
+        if (n < N) dp[0] = (uint16_t)b0;
+        if (n + 1 < N) dp[1] = (uint16_t)b1;
+        if (n + 2 < N) dp[2] = (uint16_t)b2;
+        if (n + 3 < N) dp[3] = (uint16_t)b3;
+      }
+    }
+  }
+}
+
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool KSPLIT, bool ACT, int LAYOUT,
           bool BF = false>
 __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
@@ -513,12 +666,6 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   if constexpr (BF) {
-    // BF16: no scales, so products accumulate straight in the MFMA's own
-    // accumulator.  A lane's two 16-byte chunks of a 128-byte block row hold
-    // elements 8g..8g+7 and 32+8g..32+8g+7 (g = lane / 16): exactly the
-    // operands of two 16x16x32 bf16 MFMAs, over the block's first and second
-    // 32 elements.  All sub-tiles take the first half before the second, so
-    // no MFMA waits on the one just issued.
     for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
       for (int u = 0; u < STAGES; ++u) {
@@ -527,27 +674,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // block t is in slot u
         asm volatile("" ::: "memory");
-        const uint8_t *sl = lds[u];
-        v8i bfr[TN], afr[TM];
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const int row = BM + (wn * TN + i) * 16 + fr;
-          bfr[i] = frag(sl + row * BK, row, fg);
-        }
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          const int row = (wm * TM + j) * 16 + fr;
-          afr[j] = frag(sl + row * BK, row, fg);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < TM; ++j)
-#pragma unroll
-            for (int i = 0; i < TN; ++i)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf_half(bfr[i], h),
-                                                                  bf_half(afr[j], h), acc[i][j],
-                                                                  0, 0, 0);
+        bf16_kblock<TN, TM, BM>(lds[u], wn, wm, fr, fg, acc);
       }
     }
   } else {
@@ -559,16 +686,6 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
       s_sb[h][t] = sb[(size_t)blk * Kb + kb0 + t];
     }
     __builtin_amdgcn_s_waitcnt(0);
-
-    // Product k = j * TN + i of a K block (activation group j, weight group i)
-    // comes from one MFMA; it is promoted LAG MFMAs later, when it has long
-    // landed, so the promotion FMAs issue in the shadow of the next MFMAs
-    // instead of waiting on the one just issued.  Products sit in a ring of
-    // RING registers; TN * TM is a multiple of RING, so slots and the promotion
-    // of the previous block's last products line up across blocks.  The next
-    // activation fragment and its scale are read from LDS one group ahead.
-    constexpr int LAG = 2, RING = 4;
-    static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
     v4f ring[RING];
 #pragma unroll
     for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -586,61 +703,10 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         // addresses in registers through the loop
         int so = u * SLOT;
         if (ACT) asm volatile("" : "+s"(so));
-        const uint8_t *sl = &lds[0][0] + so;
-        const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
-        const float sbv = s_sb[hsb][t];
-        v8i bfr[TN], afr[2];
-        float scb[TM];
-        // Large tiles (WGN > 1): only the first two weight fragments are read
-        // before the first MFMA and the rest one MFMA ahead of use, so the
-        // eight compute waves, released together by the barrier, do not all
-        // queue their whole fragment reads on the LDS at once (measured 1-2%
-        // on the prefill and contiguous shapes, nothing on the narrow tiles)
-        constexpr int B0 = WGN > 1 && TN > 2 ? 2 : TN;
-#pragma unroll
-        for (int i = 0; i < B0; ++i) {
-          const int row = BM + (wn * TN + i) * 16 + fr;
-          bfr[i] = frag(sl + row * BK, row, fg);
-        }
-        {
-          const int row = wm * TM * 16 + fr;
-          afr[0] = frag(sl + row * BK, row, fg);
-          scb[0] = ssl[row] * sbv;
-        }
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          if (j + 1 < TM) {
-            const int row = (wm * TM + j + 1) * 16 + fr;
-            afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
-            scb[j + 1] = ssl[row] * sbv;
-          }
-#pragma unroll
-          for (int i = 0; i < TN; ++i) {
-            if (j == 0 && i + B0 < TN) {
-              asm volatile("" ::: "memory");  // keeps the read after the MFMAs before it
-              const int row = BM + (wn * TN + i + B0) * 16 + fr;
-              bfr[i + B0] = frag(sl + row * BK, row, fg);
-            }
-            const int k = j * TN + i;
-            ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-            const int kp = k - LAG;                      // product promoted now
-            const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
-            const float sp = kp >= 0 ? scb[kq / TN] : sc_last;
-            v4f &ap = acc[kq % TN][kq / TN];
-            const v4f &pp = ring[(kq + RING) % RING];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ap[r] = __builtin_fmaf(pp[r], sp, ap[r]);
-          }
-        }
-        sc_last = scb[TM - 1];
+        fp8_kblock<WGN, TN, TM, BM>(&lds[0][0] + so, s_sb[hsb][t], wn, wm, fr, fg, acc, ring, sc_last);
       }
     }
-#pragma unroll
-    for (int k = TN * TM - LAG; k < TN * TM; ++k)  // the last block's last products
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
+    fp8_flush(acc, ring, sc_last);
   }
 
   if constexpr (ACT) {
@@ -714,13 +780,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   if (tail) {
     // this K part of a tail tile: its fp32 partial tile goes to workspace
     // slot (tail tile, split), BM x BN floats, row-major within the tile
-    float *pt = a.ws + ((size_t)(tile - a.full_tiles) * a.tail_splits + split) * (BM * BN);
-#pragma unroll
-    for (int j = 0; j < TM; ++j)
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-        *reinterpret_cast<v4f *>(pt + ((wm * TM + j) * 16 + fr) * BN + (wn * TN + i) * 16 + 4 * fg) =
-            acc[i][j];
+    store_part<TN, TM, BN>(acc, a.ws + ((size_t)(tile - a.full_tiles) * a.tail_splits + split) * (BM * BN),
+                           wn, wm, fr, fg);
     return;
   }
   if (S > 1) {
@@ -745,30 +806,237 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     }
     return;
   }
+  store_bf16<TN, TM, LAYOUT>(acc, D, a.idx, g, M, N, mvalid, m0, n0, wn, wm, fr, fg);
+}
+// ---------------------------------------------------------------------------
+// Persistent tile walk for the large tiles (dense and contiguous calls with
+// more tiles than CUs): one workgroup per CU takes items b, b + P, b + 2P, ...
+// of the same item list the tile kernel runs as separate workgroups (whole
+// tiles in XCD order, then, for dense calls, the K parts of a split last
+// wave; P is a multiple of 8, so every item of a workgroup stays on its
+// XCD).  The loader waves run one producer cursor over the workgroup's K
+// blocks of all its items, STAGES - 1 blocks ahead of the compute waves: the
+// next tile's first blocks load while the compute waves finish a tile and
+// store it.  The weight scales of each block travel in its slot with the
+// activation scales (every loader loads the same two floats, so all loaders
+// keep one count of loads per slot), so nothing is preloaded per tile.
+// Contiguous layout: each item's expert is found for all of the workgroup's
+// items at once, before any load.
+constexpr int WALK_MAXIT = 256;  // items per workgroup, at most
 
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int m = m0 + (wm * TM + j) * 16 + fr;
-    bool ok = m < mvalid;
-    if (LAYOUT == CONTIG) ok = m < M && a.idx[m] == g;
-    if (!ok) continue;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int n = n0 + (wn * TN + i) * 16 + 4 * fg;
-      uint16_t *dp = D + (size_t)m * N + n;
-      const uint32_t b0 = bf16_bits(acc[i][j][0]), b1 = bf16_bits(acc[i][j][1]);
-      const uint32_t b2 = bf16_bits(acc[i][j][2]), b3 = bf16_bits(acc[i][j][3]);
-      if ((N & 3) == 0 && n + 3 < N) {
-        *reinterpret_cast<u32x2 *>(dp) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-      } else {
-        if (n < N) dp[0] = (uint16_t)b0;
-        if (n + 1 < N) dp[1] = (uint16_t)b1;
-        if (n + 2 < N) dp[2] = (uint16_t)b2;
-        if (n + 3 < N) dp[3] = (uint16_t)b3;
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF>
+__global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
+  constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
+  constexpr int ROWS = BM + BN;
+  constexpr int SBOFF = ROWS * BK + BM * 4;          // FP8: the block's weight scales
+  constexpr int SLOT = BF ? ROWS * BK : SBOFF + 256;  // operand rows, activation scales, weight scales
+  constexpr int OCT = ROWS / 8;
+  constexpr int DMA = OCT / NLD;
+  constexpr int SG = BM / 64;
+  constexpr int SPL = BF ? 0 : (SG + NLD - 1) / NLD;
+  constexpr int PER_G = DMA + SPL + (BF ? 0 : 1);  // vector memory instructions per loader per slot
+  constexpr int NCW = WGN * WGM, NT = (NCW + NLD) * 64;
+  static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 64 == 0 &&
+                    BN <= 256 && 128 % (TN * 16) == 0 && (BM / 8) % NLD == 0,
+                "tile shape");
+  static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
+  static_assert(LAYOUT == DENSE || LAYOUT == CONTIG, "dense and contiguous layouts");
+  static_assert(LAYOUT != CONTIG || BM <= 128, "one expert per activation tile");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
+  __shared__ int s_grp[LAYOUT == CONTIG ? WALK_MAXIT : 1];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = a.M, N = a.N, K = a.K, Nb = (N + 127) / 128;
+  const int RB = BF ? 2 * K : K, Kb = RB / BK;
+  const int T = a.tiles_m * a.tiles_n;
+  const bool tsplit = LAYOUT == DENSE && a.tail_splits > 1;
+  const int F = tsplit ? a.full_tiles : T;  // whole tiles; then the tail parts
+  const int NI = F + (tsplit ? (T - F) * a.tail_splits : 0);
+  const int P = gridDim.x, b = blockIdx.x;
+  const int nit = b < NI ? (NI - b + P - 1) / P : 0;
+
+  struct Item {
+    int tile, split, m0, n0, kb0, nk;
+    bool tail;
+  };
+  // item k of this workgroup, at position b + k P of the list
+  auto item = [&](int k) {
+    constexpr int GROUPN = 4;
+    const int pos = b + k * P;
+    Item it;
+    it.tail = pos >= F;
+    if (it.tail) {
+      const int r = pos - F;
+      it.tile = F + r / a.tail_splits;
+      it.split = r % a.tail_splits;
+    } else {
+      const int x = pos % 8, l = pos / 8, per = F / 8, rem = F % 8;
+      it.tile = x * per + min(x, rem) + l;
+      it.split = 0;
+    }
+    const int gsz = GROUPN * a.tiles_m, grp = it.tile / gsz, in = it.tile % gsz;
+    const int gw = min(GROUPN, a.tiles_n - grp * GROUPN);
+    it.n0 = (grp * GROUPN + in % gw) * BN;
+    it.m0 = (in / gw) * BM;
+    const int kbps = it.tail ? a.tail_kb : Kb;
+    it.kb0 = it.split * kbps;
+    it.nk = max(0, min(Kb - it.kb0, kbps));
+    return it;
+  };
+
+  if (LAYOUT == CONTIG) {
+    // each item's expert: the largest valid index among its rows (one expert
+    // per 128-row block by contract; every row is checked again at store
+    // time), -1 when they are all padding
+    for (int k = tid; k < nit; k += NT) s_grp[k] = -1;
+    __syncthreads();
+    for (int e = tid; e < nit * BM; e += NT) {
+      const int m = item(e / BM).m0 + e % BM;
+      if (m < M) {
+        const int v = a.idx[m];
+        if (v >= 0 && v < a.G) atomicMax(&s_grp[e / BM], v);
       }
+    }
+    __syncthreads();
+  }
+  // expert of item k (0 for dense), -1: nothing to do
+  auto group = [&](int k) { return LAYOUT == CONTIG ? s_grp[k] : 0; };
+
+  if (wave >= NCW) {
+    // ---------------- loader waves ----------------
+    const int L = wave - NCW, lane = tid & 63;
+    constexpr int QA = BM / 8 / NLD;  // loads q < QA are activation row groups, the rest weights
+    __amdgpu_buffer_rsrc_t ra = rsrc(a.A, (uint32_t)M * RB), rb = ra, rs = ra, rsb = ra;
+    if (!BF) rs = rsrc(a.sa, (uint32_t)M * Kb * 4);
+    uint32_t off[DMA], soff[SPL > 0 ? SPL : 1], sboff = OOB;
+    int sdst[SPL > 0 ? SPL : 1];
+#pragma unroll
+    for (int jj = 0; jj < SPL; ++jj) sdst[jj] = ROWS * BK + ((L + NLD * jj) % SG) * 256;
+    int pk = -1, pt = 0, pnk = 0, pkb0 = 0;  // producer: item, block in it, its count and first block
+    // move the producer to the next item with work; past the last one, every
+    // load goes out of range (zeros, no traffic), so each slot still counts
+    // PER_G loads per loader
+    auto advance = [&]() {
+      for (++pk; pk < nit; ++pk) {
+        const int g = group(pk);
+        if (g < 0) continue;
+        const Item it = item(pk);
+        if (LAYOUT == CONTIG) {
+          rb = rsrc(a.B + (size_t)g * N * RB, (uint32_t)N * RB);
+          if (!BF) rsb = rsrc(a.sb + (size_t)g * Nb * Kb, (uint32_t)Nb * Kb * 4);
+        } else {
+          rb = rsrc(a.B, (uint32_t)N * RB);
+          if (!BF) rsb = rsrc(a.sb, (uint32_t)Nb * Kb * 4);
+        }
+        // q-th row-group load: rows (L + NLD q) * 8 .. + 7 of the slot; lane l
+        // -> row + l / 8, physical chunk l % 8 holding logical chunk
+        // (l % 8) ^ key(row); rows past M or N read out of range
+#pragma unroll
+        for (int q = 0; q < DMA; ++q) {
+          const int r = (L + NLD * q) * 8 + (lane >> 3);
+          const int col = (lane & 7) ^ row_key(r);
+          const int grow = q < QA ? it.m0 + r : it.n0 + r - BM;
+          off[q] = grow < (q < QA ? M : N) ? (uint32_t)grow * RB + col * 16 : OOB;
+        }
+        if (!BF) {
+#pragma unroll
+          for (int jj = 0; jj < SPL; ++jj) {
+            const int m = it.m0 + ((L + NLD * jj) % SG) * 64 + lane;
+            soff[jj] = m < M ? (uint32_t)m * 4 : OOB;
+          }
+          // lane h < BN / 128: the scale row of the tile's h-th 128-row weight block
+          sboff = lane < BN / 128 ? (uint32_t)min(it.n0 / 128 + lane, Nb - 1) * Kb * 4 : OOB;
+        }
+        pkb0 = it.kb0;
+        pnk = it.nk;
+        pt = 0;
+        return;
+      }
+      pnk = 0;
+      pt = 0;
+    };
+    auto produce = [&](int s) {
+      if (pt == pnk && pk < nit) advance();
+      const bool real = pt < pnk;
+      const uint32_t kb = real ? (uint32_t)(pkb0 + pt) : 0u;
+      uint8_t *sl = &lds[0][0] + s * SLOT;
+#pragma unroll
+      for (int q = 0; q < DMA; ++q) dma16(q < QA ? ra : rb, real ? off[q] + kb * BK : OOB, sl + (L + NLD * q) * 1024);
+#pragma unroll
+      for (int jj = 0; jj < SPL; ++jj) dma4(rs, real ? soff[jj] + kb * M * 4 : OOB, sl + sdst[jj]);
+      if (!BF) dma4(rsb, real ? sboff + kb * 4 : OOB, sl + SBOFF);
+      pt += real ? 1 : 0;
+    };
+    int ps = 0;  // slot the producer fills next
+#pragma unroll
+    for (int q = 0; q < STAGES - 1; ++q) {
+      produce(ps);
+      ps = ps + 1 == STAGES ? 0 : ps + 1;
+    }
+    for (int k = 0; k < nit; ++k) {
+      if (group(k) < 0) continue;
+      const int nk = item(k).nk;
+      for (int t = 0; t < nk; ++t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_G * (STAGES - 2)));  // my loads of this block landed
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // ... and everyone's; all compute waves are past the previous block
+        asm volatile("" ::: "memory");
+        produce(ps);
+        ps = ps + 1 == STAGES ? 0 : ps + 1;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int lane = tid & 63, fr = lane & 15, fg = lane >> 4;
+  const int wn = wave % WGN, wm = wave / WGN;
+  const int hsb = (wn * TN * 16) / 128;  // which of the slot's weight scales this wave's rows use
+  int cs = 0;                            // slot of the next block
+  for (int k = 0; k < nit; ++k) {
+    const int g = group(k);
+    if (g < 0) continue;  // all padding: nothing loaded, nothing written
+    const Item it = item(k);
+    v4f acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF) {
+      for (int t = 0; t < it.nk; ++t) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // this item's block t is in slot cs
+        asm volatile("" ::: "memory");
+        bf16_kblock<TN, TM, BM>(&lds[0][0] + cs * SLOT, wn, wm, fr, fg, acc);
+        cs = cs + 1 == STAGES ? 0 : cs + 1;
+      }
+    } else {
+      v4f ring[RING];
+#pragma unroll
+      for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
+      float sc_last = 0.f;
+      for (int t = 0; t < it.nk; ++t) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // this item's block t is in slot cs
+        asm volatile("" ::: "memory");
+        const uint8_t *sl = &lds[0][0] + cs * SLOT;
+        const float sbv = reinterpret_cast<const float *>(sl + SBOFF)[hsb];
+        fp8_kblock<WGN, TN, TM, BM>(sl, sbv, wn, wm, fr, fg, acc, ring, sc_last);
+        cs = cs + 1 == STAGES ? 0 : cs + 1;
+      }
+      fp8_flush(acc, ring, sc_last);
+    }
+    if (it.tail) {
+      store_part<TN, TM, BN>(acc, a.ws + ((size_t)(it.tile - F) * a.tail_splits + it.split) * (BM * BN),
+                             wn, wm, fr, fg);
+    } else {
+      store_bf16<TN, TM, LAYOUT>(acc, a.D, a.idx, g, M, N, M, it.m0, it.n0, wn, wm, fr, fg);
     }
   }
 }
+
 // Split-K reduction (decode): D[m][n] = bf16(sum over s, in split order, of
 // ws[s][m][n]).  One thread per 4 consecutive columns of a row; the planes
 // are fetched 8 at a time with buffer loads (planes past S read out of range:
@@ -980,6 +1248,41 @@ int launch(Args a, int groups, hipStream_t stream) {
   return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
+// Workgroups of the persistent walk: the device's CUs, rounded down to a
+// multiple of the 8 XCDs (one workgroup per CU: the walk's ring takes most
+// of a CU's LDS).  Cached per device.
+int walk_workgroups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev].load(std::memory_order_relaxed) > 0)
+    return cache[dev].load(std::memory_order_relaxed);
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  n = n / 8 * 8;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+// The walk for calls with more tiles than CUs and operand rows of at most
+// 8 KB (FP8 K <= 8192, BF16 K <= 4096).  Measured against one workgroup per
+// tile: 9% faster at FP8 K = 1536, 2-4% on the contiguous K = 7168 calls,
+// 2-3% slower at K = 16384 and 18432, where a tile's fixed costs are a small
+// share of its time and the walk's runtime slot indexing costs a little in
+// every block.  FP8GEMM_WALK=0 (tuning override) turns it off.
+bool walk_enabled(int row_bytes) {
+  const char *e = getenv("FP8GEMM_WALK");
+  return !(e && e[0] == '0') && row_bytes <= 8192;
+}
+
+// a.tiles_m / tiles_n and the tail fields set; `items` work items in all
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF>
+hipError_t launch_walk(Args &a, int P, hipStream_t stream) {
+  void *kargs[] = {&a};
+  return hipLaunchKernel(
+      reinterpret_cast<const void *>(&walk_kernel<WGN, WGM, TN, TM, STAGES, NLD, LAYOUT, BF>),
+      dim3(P), dim3((WGN * WGM + NLD) * 64), kargs, 0, stream);
+}
+
 // Dense M > 128 with one large tile per CU.  When the tiles leave a last
 // wave of R <= 128 tiles for the 256 CUs, those R tiles are split over K into
 // S = min(8, 256 / R) parts (each at least 4 K blocks) that run as the last
@@ -994,25 +1297,54 @@ int launch_dense_large(Args a, hipStream_t stream) {
   while (S > 1 && cdiv(Kb, S) < 4) --S;
   const Workspace *w = S > 1 ? workspace(stream) : nullptr;
   if (S > 1 && (!w || (size_t)R * S * BM * BN > WS_FLOATS)) S = 1;
-  if (S <= 1) return launch_tile<WGN, WGM, TN, TM, STAGES, NLD, DENSE, false, false, BF>(a, 1, stream);
-  const int kb = cdiv(Kb, S);
+  // more tiles than CUs: the persistent walk over the same items
+  const int P = walk_workgroups();
+  const bool walk = walk_enabled(BF ? 2 * a.K : a.K) && P >= 8 && T > P;
   a.tiles_m = tiles_m;
   a.tiles_n = tiles_n;
   a.splits = 1;
   a.kb_per_split = Kb;
+  if (S <= 1) {
+    if (!walk) return launch_tile<WGN, WGM, TN, TM, STAGES, NLD, DENSE, false, false, BF>(a, 1, stream);
+    return launch_walk<WGN, WGM, TN, TM, STAGES, NLD, DENSE, BF>(a, P, stream) == hipSuccess
+               ? FP8GEMM_OK
+               : FP8GEMM_LAUNCH_FAILED;
+  }
+  const int kb = cdiv(Kb, S);
   a.full_tiles = T - R;
   a.tail_splits = cdiv(Kb, kb);
   a.tail_kb = kb;
   a.ws = w->part;
-  void *kargs[] = {&a};
-  hipError_t er = hipLaunchKernel(
-      reinterpret_cast<const void *>(
-          &tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, false, false, DENSE, BF>),
-      dim3(a.full_tiles + R * a.tail_splits), dim3((WGN * WGM + NLD) * 64), kargs, 0, stream);
+  hipError_t er;
+  if (walk) {
+    er = launch_walk<WGN, WGM, TN, TM, STAGES, NLD, DENSE, BF>(a, P, stream);
+  } else {
+    void *kargs[] = {&a};
+    er = hipLaunchKernel(
+        reinterpret_cast<const void *>(
+            &tile_kernel<WGN, WGM, TN, TM, STAGES, NLD, false, false, DENSE, BF>),
+        dim3(a.full_tiles + R * a.tail_splits), dim3((WGN * WGM + NLD) * 64), kargs, 0, stream);
+  }
   if (er != hipSuccess) return FP8GEMM_LAUNCH_FAILED;
   hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(R * (BM * BN / 4) / 256), dim3(256), 0, stream,
                      a.ws, a.D, a.M, a.N, a.full_tiles, a.tail_splits, tiles_m, tiles_n);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+}
+
+// Contiguous layout, 256 x 128 tiles: the persistent walk when there are
+// more tiles than CUs (and few enough per workgroup for its expert table)
+template <bool BF>
+int launch_contig_large(Args a, hipStream_t stream) {
+  const int P = walk_workgroups();
+  a.tiles_m = cdiv(a.M, 128);
+  a.tiles_n = cdiv(a.N, 256);
+  const int T = a.tiles_m * a.tiles_n;
+  if (!walk_enabled(BF ? 2 * a.K : a.K) || P < 8 || T <= P || cdiv(T, P) > WALK_MAXIT)
+    return launch_tile<4, 2, 4, 4, 3, 4, CONTIG, false, false, BF>(a, 1, stream);
+  a.splits = 1;
+  a.kb_per_split = (BF ? 2 * a.K : a.K) / BK;
+  return launch_walk<4, 2, 4, 4, 3, 4, CONTIG, BF>(a, P, stream) == hipSuccess ? FP8GEMM_OK
+                                                                              : FP8GEMM_LAUNCH_FAILED;
 }
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -1072,7 +1404,7 @@ int grouped_contiguous(const void *A, const float *sa, const void *B, const floa
   const char *e = getenv("FP8GEMM_LARGE");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (e && e[0] == '6') return launch_tile<4, 1, 4, 8, 3, 2, CONTIG>(a, 1, s);
-  return launch_tile<4, 2, 4, 4, 3, 4, CONTIG>(a, 1, s);
+  return launch_contig_large<false>(a, s);
 }
 
 int grouped_masked(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -1175,8 +1507,7 @@ int grouped_contiguous_bf16(const void *A, const void *B, void *D, int M, int N,
   if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), nullptr, static_cast<const uint8_t *>(B), nullptr,
          static_cast<uint16_t *>(D), M, N, K, G, m_indices, 0, 0, 1, 2 * K / BK, nullptr};
-  return launch_tile<4, 2, 4, 4, 3, 4, CONTIG, false, false, true>(
-      a, 1, static_cast<hipStream_t>(stream));
+  return launch_contig_large<true>(a, static_cast<hipStream_t>(stream));
 }
 
 int grouped_masked_bf16(const void *A, const void *B, void *D, int M, int N, int K, int G,

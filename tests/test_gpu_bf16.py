@@ -113,6 +113,33 @@ def test_dense_prefill_shape_sampled_rows():
     assert_close(D[rows], oracle.gemm_bf16("dense", np.ascontiguousarray(A[rows]), B), "bf16 prefill rows")
 
 
+@pytest.mark.parametrize("walk", ["default", "0"])
+def test_dense_persistent_walk(walk, monkeypatch):
+    """9 x 30 = 270 tiles of 128 x 256: the persistent walk, with a tail split
+    of the last 14 tiles, and one workgroup per tile."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    M, N, K = 2304, 3840, 512
+    announce(f"bf16 walk {walk} dense {M}x{N}x{K}")
+    A, B = rand_bf16(11050, (M, K)), rand_bf16(11051, (N, K), 0.5)
+    assert_close(gpu_dense(A, B), oracle.gemm_bf16("dense", A, B), f"bf16 walk {walk}")
+
+
+@pytest.mark.parametrize("walk", ["default", "0"])
+def test_contiguous_persistent_walk(walk, monkeypatch):
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    G, rows, N, K = 4, 128 * 18, 4096, 256  # 18 x 16 = 288 tiles
+    announce(f"bf16 walk {walk} contiguous G={G} rows={rows}")
+    idx, _ = synth.contiguous_indices(11070, G, rows, False)
+    A, B = rand_bf16(11071, (rows, K)), rand_bf16(11072, (G, N, K), 0.5)
+    got = gpu_contig(A, B, idx)
+    want = oracle.gemm_bf16("contiguous", A, B, idx, out=np.full((rows, N), SENTINEL, np.uint16))
+    live = (idx >= 0) & (idx < G)
+    assert (got[~live] == SENTINEL).all(), "a padding row was written"
+    assert_close(got[live], want[live], f"bf16 walk {walk} contiguous")
+
+
 # ------------------------------------------------------------- grouped ----
 
 

@@ -272,6 +272,38 @@ def test_dense_tail_split_sampled():
     assert_close(out[pm, pn], ref, f"tail {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("walk", ["default", "0"])
+def test_dense_persistent_walk_full(walk, monkeypatch):
+    """More 256 x 128 tiles than CUs: one workgroup per CU walks several tiles
+    (ragged in M and N); FP8GEMM_WALK=0 runs the same problem one workgroup
+    per tile."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    M, N, K = 1100, 7400, 256  # 9 x 29 = 261 tiles
+    seed = 3700
+    announce(f"walk {walk} dense {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K)
+    assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), f"walk {M}x{N}x{K}")
+
+
+def test_dense_persistent_walk_with_tail_sampled():
+    """261 tiles, K = 2048: 256 whole tiles and 5 tiles in 4 K parts, walked
+    by 256 workgroups (the parts after each workgroup's whole tile)."""
+    M, N, K = 1100, 7400, 2048
+    seed = 3710
+    announce(f"walk+tail dense {M}x{N}x{K} seed {seed}")
+    d = W.dense(seed, M, N, K)
+    out = gpu_dense(d)
+    assert (out != SENTINEL).all()
+    rng = np.random.default_rng(seed)
+    pm, pn = sample_points(rng, M, N, 3000)
+    # the tail tiles are the walk's last five: rows 512..1099, columns 7168..7399
+    pm = np.concatenate([pm, rng.integers(512, M, 3000)])
+    pn = np.concatenate([pn, rng.integers(7168, N, 3000)])
+    ref = oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn)
+    assert_close(out[pm, pn], ref, f"walk+tail {M}x{N}x{K}")
+
+
 # ------------------------------------------------------------- contiguous ---
 
 
@@ -346,6 +378,23 @@ def test_contiguous_routing_probe_exact():
     out = gpu_contig(d)
     ref = oracle.grouped_contiguous(A, sa, B, sb, idx, np.full((M, N), SENTINEL, np.uint16))
     assert (out == ref).all()
+
+
+@pytest.mark.parametrize("walk", ["default", "0"])
+def test_contiguous_persistent_walk_full(walk, monkeypatch):
+    """20 expert blocks x 17 weight tiles = 340 tiles, uneven segments with
+    padding rows: the persistent walk (each workgroup's experts found up
+    front) and one workgroup per tile."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    d = W.contiguous(4170, 5, 128 * 20, 4300, 256, uniform=False)
+    announce(f"walk {walk} contiguous G=5 2560x4300x256")
+    out = gpu_contig(d)
+    ref = oracle.grouped_contiguous(d["A"], d["sa"], d["B"], d["sb"], d["m_indices"],
+                                    np.full((d["M"], d["N"]), SENTINEL, np.uint16))
+    pad = d["m_indices"] < 0
+    assert (out[pad] == SENTINEL).all() and (out[~pad] != SENTINEL).all()
+    assert_close(out[~pad], ref[~pad], f"walk {walk} contiguous")
 
 
 @pytest.mark.parametrize("case", range(len(W.CONTIG_CASES)))
