@@ -1169,16 +1169,17 @@ int launch_tile(Args a, int groups, hipStream_t stream) {
 // Dense GEMM with M <= 128 (decode): the tile kernel with a deep ring, four
 // loader waves, 64 weight rows per tile and a K split sized so that the
 // (split, tile) items cover the chip.
-// Optional override for tuning sweeps: FP8GEMM_DECODE="bn,stages,splits".
+// Optional override for tuning sweeps: FP8GEMM_DECODE="bn,stages,splits[,waves]".
 struct DecodeCfg {
-  int bn, stages, splits;
+  int bn, stages, splits, waves;
 };
 
-// Instances built: (bn, stages) in {(64,4), (64,6), (128,4)} for both
-// activation tile heights.
-bool decode_built(int bn, int stages, int bm) {
-  (void)bm;
-  return (bn == 64 && (stages == 4 || stages == 6)) || (bn == 128 && stages == 4);
+// Instances built: four compute waves with (bn, stages) in {(64,4), (64,6),
+// (128,4)} for both activation tile heights; eight compute waves with four
+// slots for bn = 128, and for bn = 64 with 128 activation rows.
+bool decode_built(int bn, int stages, int bm, int waves) {
+  if (waves == 8) return stages == 4 && (bn == 128 || (bn == 64 && bm == 128));
+  return waves == 4 && ((bn == 64 && (stages == 4 || stages == 6)) || (bn == 128 && stages == 4));
 }
 
 // Default (measured on MI355X over the decode shapes, weights streamed from
@@ -1187,17 +1188,22 @@ bool decode_built(int bn, int stages, int bm) {
 // byte); a K split only when the tiles alone leave CUs idle, with (tiles x
 // splits) kept within one wave of 256 workgroups and at least 9 K blocks per
 // split, since the partial planes and their reduction cost about 3 us.
-DecodeCfg decode_config(int M, int N, int Kb) {
+DecodeCfg decode_config(int M, int N, int Kb, bool bf) {
   const int bm = M <= 64 ? 64 : 128;
   const char *e = getenv("FP8GEMM_DECODE");
-  DecodeCfg o;
-  if (e && sscanf(e, "%d,%d,%d", &o.bn, &o.stages, &o.splits) == 3 && o.splits >= 1 &&
-      decode_built(o.bn, o.stages, bm))
+  DecodeCfg o{0, 0, 0, 4};
+  if (e && sscanf(e, "%d,%d,%d,%d", &o.bn, &o.stages, &o.splits, &o.waves) >= 3 && o.splits >= 1 &&
+      decode_built(o.bn, o.stages, bm, o.waves))
     return o;
   const int tiles64 = cdiv(N, 64);
-  DecodeCfg c{tiles64 >= 384 ? 128 : 64, 4, 1};
+  DecodeCfg c{tiles64 >= 384 ? 128 : 64, 4, 1, 4};
   const int tiles = cdiv(N, c.bn) * cdiv(M, bm);
   c.splits = std::max(1, std::min(256 / std::max(tiles, 1), Kb / 9));
+  // eight compute waves (two per SIMD, so one's promotion FMAs overlap the
+  // other's MFMAs) where the tile has the rows for them and K is not split:
+  // 2-4% on 24576x1536 and on 128x7168x2048, slower with a K split
+  // (FP8 only: BF16 has no promotion)
+  if (!bf && c.splits == 1 && decode_built(c.bn, 4, bm, 8)) c.waves = 8;
   return c;
 }
 
@@ -1205,7 +1211,7 @@ DecodeCfg decode_config(int M, int N, int Kb) {
 template <bool BF>
 int run_decode(Args a, hipStream_t stream) {
   const int Kb = (BF ? 2 * a.K : a.K) / BK;
-  DecodeCfg c = decode_config(a.M, a.N, Kb);
+  DecodeCfg c = decode_config(a.M, a.N, Kb, BF);
   const int bm = a.M <= 64 ? 64 : 128;
   int splits = std::max(1, std::min(c.splits, std::max(Kb, 1)));
   const int kps = Kb > 0 ? cdiv(Kb, splits) : 0;
@@ -1222,8 +1228,15 @@ int run_decode(Args a, hipStream_t stream) {
     }
   }
   int st = FP8GEMM_LAUNCH_FAILED;  // unreachable: decode_config returns built instances only
+  if (c.waves == 8) {
+    if (c.bn == 128)
+      st = bm == 64 ? launch_tile<2, 4, 4, 1, 4, 4, DENSE, true, false, BF>(a, 1, stream)
+                    : launch_tile<2, 4, 4, 2, 4, 4, DENSE, true, false, BF>(a, 1, stream);
+    else
+      st = launch_tile<2, 4, 2, 2, 4, 4, DENSE, true, false, BF>(a, 1, stream);
+  }
 #define DEC(BN_, ST_)                                                                     \
-  if (c.bn == BN_ && c.stages == ST_)                                                     \
+  if (c.waves == 4 && c.bn == BN_ && c.stages == ST_)                                     \
     st = bm == 64 ? launch_tile<1, 4, BN_ / 16, 1, ST_, 4, DENSE, true, false, BF>(a, 1, stream) \
                   : launch_tile<1, 4, BN_ / 16, 2, ST_, 4, DENSE, true, false, BF>(a, 1, stream);
   DEC(64, 4)
