@@ -1435,13 +1435,15 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K > 20480) return launch<64, 128, MASKED>(a, G, s);
   // measured on MI355X (G = 16, 256-row capacity, counts ~ U[0, 256]):
-  // 128 weight rows by 128 activation rows, four loader waves, four slots;
+  // 128 weight rows by 128 activation rows, eight compute waves (2-3% over
+  // four: two per SIMD overlap promotion FMAs with MFMAs), four loader
+  // waves, four slots;
   // 64-row activation tiles when the hint says counts are small; for short K
   // (K = 2048: 20% faster, but 9% slower at K = 7168) 256 weight rows, which
   // halve the activation re-reads and the tiles' fixed costs
   if (expected_m <= 64) return launch_tile<1, 4, 8, 1, 4, 4, MASKED>(a, G, s);
   if (K <= 4096) return launch_tile<4, 2, 4, 4, 3, 4, MASKED>(a, G, s);
-  return launch_tile<1, 4, 8, 2, 4, 4, MASKED>(a, G, s);
+  return launch_tile<2, 4, 4, 2, 4, 4, MASKED>(a, G, s);
 }
 
 // Grouped GEMM with B_g = [W_gate; W_up] (N = 2I rows) and the SwiGLU and
