@@ -821,8 +821,12 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
 // activation scales (every loader loads the same two floats, so all loaders
 // keep one count of loads per slot), so nothing is preloaded per tile.
 // Contiguous layout: each item's expert is found for all of the workgroup's
-// items at once, before any load.
-constexpr int WALK_MAXIT = 256;  // items per workgroup, at most
+// items at once, before any load.  Masked layout: the list holds only the
+// live tiles, expert by expert (ceil(masked_m[g] / BM) activation tiles by
+// the weight tiles); every workgroup builds the experts' offsets into it from
+// masked_m on the device, and finds an item's expert by binary search.
+constexpr int WALK_MAXIT = 256;  // items per workgroup, at most (contiguous)
+constexpr int WALK_MAXG = 512;   // experts, at most (masked)
 
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF>
 __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
@@ -840,24 +844,54 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
                     BN <= 256 && 128 % (TN * 16) == 0 && (BM / 8) % NLD == 0,
                 "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
-  static_assert(LAYOUT == DENSE || LAYOUT == CONTIG, "dense and contiguous layouts");
   static_assert(LAYOUT != CONTIG || BM <= 128, "one expert per activation tile");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ int s_grp[LAYOUT == CONTIG ? WALK_MAXIT : 1];
+  // masked: items before expert g's (s_pre[g]) and its valid rows (s_mv[g])
+  __shared__ int s_pre[LAYOUT == MASKED ? WALK_MAXG + 1 : 1];
+  __shared__ int s_mv[LAYOUT == MASKED ? WALK_MAXG : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = a.M, N = a.N, K = a.K, Nb = (N + 127) / 128;
   const int RB = BF ? 2 * K : K, Kb = RB / BK;
+  if (LAYOUT == MASKED) {
+    // the live tiles: expert g has ceil(min(max(masked_m[g], 0), M) / BM)
+    // activation tiles by tiles_n weight tiles; a wave-wide prefix sum over
+    // the experts, 64 at a time, gives each expert's first item
+    if (wave == 0) {
+      const int lane = tid & 63;
+      int carry = 0;
+      for (int base = 0; base < a.G; base += 64) {
+        const int g = base + lane;
+        int c = 0;
+        if (g < a.G) {
+          const int v = a.idx[g], mv = v < 0 ? 0 : (v > M ? M : v);
+          s_mv[g] = mv;
+          c = (mv + BM - 1) / BM * a.tiles_n;
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(c, d, 64);
+          if (lane >= d) c += y;
+        }
+        if (g < a.G) s_pre[g + 1] = carry + c;
+        carry += __shfl(c, 63, 64);
+      }
+      if (lane == 0) s_pre[0] = 0;
+    }
+    __syncthreads();
+  }
   const int T = a.tiles_m * a.tiles_n;
   const bool tsplit = LAYOUT == DENSE && a.tail_splits > 1;
-  const int F = tsplit ? a.full_tiles : T;  // whole tiles; then the tail parts
+  // whole tiles (masked: the live ones, counted on the device); then the tail parts
+  const int F = LAYOUT == MASKED ? s_pre[a.G] : tsplit ? a.full_tiles : T;
   const int NI = F + (tsplit ? (T - F) * a.tail_splits : 0);
   const int P = gridDim.x, b = blockIdx.x;
   const int nit = b < NI ? (NI - b + P - 1) / P : 0;
 
   struct Item {
-    int tile, split, m0, n0, kb0, nk;
+    int tile, split, m0, n0, kb0, nk, g, mvalid;
     bool tail;
   };
   // item k of this workgroup, at position b + k P of the list
@@ -875,7 +909,23 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
       it.tile = x * per + min(x, rem) + l;
       it.split = 0;
     }
-    const int gsz = GROUPN * a.tiles_m, grp = it.tile / gsz, in = it.tile % gsz;
+    int tiles_m = a.tiles_m, tile = it.tile;
+    it.g = 0;
+    it.mvalid = M;
+    if (LAYOUT == MASKED) {
+      // the expert holding live tile `tile`: the last g with s_pre[g] <= tile
+      int lo = 0, hi = a.G - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= tile) lo = mid;
+        else hi = mid - 1;
+      }
+      it.g = lo;
+      it.mvalid = s_mv[lo];
+      tiles_m = (s_pre[lo + 1] - s_pre[lo]) / a.tiles_n;
+      tile -= s_pre[lo];
+    }
+    const int gsz = GROUPN * tiles_m, grp = tile / gsz, in = tile % gsz;
     const int gw = min(GROUPN, a.tiles_n - grp * GROUPN);
     it.n0 = (grp * GROUPN + in % gw) * BN;
     it.m0 = (in / gw) * BM;
@@ -919,10 +969,14 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
     // PER_G loads per loader
     auto advance = [&]() {
       for (++pk; pk < nit; ++pk) {
-        const int g = group(pk);
-        if (g < 0) continue;
+        if (group(pk) < 0) continue;
         const Item it = item(pk);
-        if (LAYOUT == CONTIG) {
+        const int g = LAYOUT == MASKED ? it.g : group(pk);
+        if (LAYOUT == MASKED) {
+          ra = rsrc(a.A + (size_t)g * M * RB, (uint32_t)M * RB);
+          if (!BF) rs = rsrc(a.sa + (size_t)g * Kb * M, (uint32_t)M * Kb * 4);
+        }
+        if (LAYOUT != DENSE) {
           rb = rsrc(a.B + (size_t)g * N * RB, (uint32_t)N * RB);
           if (!BF) rsb = rsrc(a.sb + (size_t)g * Nb * Kb, (uint32_t)Nb * Kb * 4);
         } else {
@@ -937,13 +991,13 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
           const int r = (L + NLD * q) * 8 + (lane >> 3);
           const int col = (lane & 7) ^ row_key(r);
           const int grow = q < QA ? it.m0 + r : it.n0 + r - BM;
-          off[q] = grow < (q < QA ? M : N) ? (uint32_t)grow * RB + col * 16 : OOB;
+          off[q] = grow < (q < QA ? it.mvalid : N) ? (uint32_t)grow * RB + col * 16 : OOB;
         }
         if (!BF) {
 #pragma unroll
           for (int jj = 0; jj < SPL; ++jj) {
             const int m = it.m0 + ((L + NLD * jj) % SG) * 64 + lane;
-            soff[jj] = m < M ? (uint32_t)m * 4 : OOB;
+            soff[jj] = m < it.mvalid ? (uint32_t)m * 4 : OOB;
           }
           // lane h < BN / 128: the scale row of the tile's h-th 128-row weight block
           sboff = lane < BN / 128 ? (uint32_t)min(it.n0 / 128 + lane, Nb - 1) * Kb * 4 : OOB;
@@ -996,9 +1050,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
   const int hsb = (wn * TN * 16) / 128;  // which of the slot's weight scales this wave's rows use
   int cs = 0;                            // slot of the next block
   for (int k = 0; k < nit; ++k) {
-    const int g = group(k);
-    if (g < 0) continue;  // all padding: nothing loaded, nothing written
+    if (group(k) < 0) continue;  // all padding: nothing loaded, nothing written
     const Item it = item(k);
+    const int g = LAYOUT == MASKED ? it.g : group(k);
     v4f acc[TN][TM];
 #pragma unroll
     for (int i = 0; i < TN; ++i)
@@ -1032,7 +1086,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
       store_part<TN, TM, BN>(acc, a.ws + ((size_t)(it.tile - F) * a.tail_splits + it.split) * (BM * BN),
                              wn, wm, fr, fg);
     } else {
-      store_bf16<TN, TM, LAYOUT>(acc, a.D, a.idx, g, M, N, M, it.m0, it.n0, wn, wm, fr, fg);
+      store_bf16<TN, TM, LAYOUT>(acc, a.D + (LAYOUT == MASKED ? (size_t)g * M * N : 0), a.idx, g, M,
+                                 N, it.mvalid, it.m0, it.n0, wn, wm, fr, fg);
     }
   }
 }
@@ -1281,10 +1336,15 @@ int walk_workgroups() {
 // tile: 9% faster at FP8 K = 1536, 2-4% on the contiguous K = 7168 calls,
 // 2-3% slower at K = 16384 and 18432, where a tile's fixed costs are a small
 // share of its time and the walk's runtime slot indexing costs a little in
-// every block.  FP8GEMM_WALK=0 (tuning override) turns it off.
-bool walk_enabled(int row_bytes) {
+// every block.  Masked calls keep one workgroup per (tile, expert) unless
+// FP8GEMM_WALK=2: their walk over the live tiles measured the same per call
+// and up to 3% slower over the two masked workload calls.  FP8GEMM_WALK=0
+// turns the walk off everywhere (tuning overrides).
+bool walk_enabled(int row_bytes, bool masked = false) {
   const char *e = getenv("FP8GEMM_WALK");
-  return !(e && e[0] == '0') && row_bytes <= 8192;
+  if (e && e[0] == '0') return false;
+  if (masked && !(e && e[0] == '2')) return false;
+  return row_bytes <= 8192;
 }
 
 // a.tiles_m / tiles_n and the tail fields set; `items` work items in all
@@ -1442,8 +1502,21 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   // (K = 2048: 20% faster, but 9% slower at K = 7168) 256 weight rows, which
   // halve the activation re-reads and the tiles' fixed costs
   if (expected_m <= 64) return launch_tile<1, 4, 8, 1, 4, 4, MASKED>(a, G, s);
-  if (K <= 4096) return launch_tile<4, 2, 4, 4, 3, 4, MASKED>(a, G, s);
-  return launch_tile<2, 4, 4, 2, 4, 4, MASKED>(a, G, s);
+  // the persistent walk over the live tiles (up to WALK_MAXG experts)
+  const int P = walk_workgroups();
+  const bool walk = walk_enabled(K, true) && P >= 8 && G <= WALK_MAXG;
+  if (K <= 4096) {
+    if (!walk) return launch_tile<4, 2, 4, 4, 3, 4, MASKED>(a, G, s);
+    a.tiles_m = cdiv(M, 128);
+    a.tiles_n = cdiv(N, 256);
+    return launch_walk<4, 2, 4, 4, 3, 4, MASKED, false>(a, P, s) == hipSuccess ? FP8GEMM_OK
+                                                                               : FP8GEMM_LAUNCH_FAILED;
+  }
+  if (!walk) return launch_tile<2, 4, 4, 2, 4, 4, MASKED>(a, G, s);
+  a.tiles_m = cdiv(M, 128);
+  a.tiles_n = cdiv(N, 128);
+  return launch_walk<2, 4, 4, 2, 4, 4, MASKED, false>(a, P, s) == hipSuccess ? FP8GEMM_OK
+                                                                             : FP8GEMM_LAUNCH_FAILED;
 }
 
 // Grouped GEMM with B_g = [W_gate; W_up] (N = 2I rows) and the SwiGLU and

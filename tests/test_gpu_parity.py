@@ -454,6 +454,29 @@ def test_masked_count_sweep_and_hint():
         outs.append(out)
 
 
+@pytest.mark.parametrize("walk", ["2", "default"])
+@pytest.mark.parametrize("G,M,N,K", [(70, 130, 260, 256),    # more experts than one wave scans at once
+                                     (12, 130, 300, 4224)])  # K > 4096: the 128 x 128 tile
+def test_masked_persistent_walk_full(G, M, N, K, walk, monkeypatch):
+    """The walk over the live tiles only (FP8GEMM_WALK=2; counts clamped to
+    [0, M], zero, past M, one row past a tile) and the default, one workgroup
+    per (tile, expert)."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    seed = 5300 + G
+    d = W.masked(seed, G, M, N, K)
+    counts = np.random.default_rng(seed).integers(-5, M + 10, G).astype(np.int32)
+    counts[:4] = [0, M, 129, M + 7]
+    d["masked_m"] = counts
+    announce(f"walk {walk} masked G={G} {M}x{N}x{K} seed {seed}")
+    out = gpu_masked(d, expected_m=128)
+    ref = oracle.grouped_masked(d["A"], d["sa"], d["B"], d["sb"], counts,
+                                np.full((G, M, N), SENTINEL, np.uint16))
+    written = np.arange(M)[None, :] < np.clip(counts, 0, M)[:, None]
+    assert (out[~written] == SENTINEL).all() and (out[written] != SENTINEL).all()
+    assert_close(out[written], ref[written], f"walk {walk} masked G={G}")
+
+
 @pytest.mark.parametrize("case", range(len(W.MASKED_CASES)))
 def test_masked_workload_sampled(case):
     G, M, N, K = W.MASKED_CASES[case]
