@@ -347,7 +347,7 @@ def profile_commands(workload, out="gpurun_out/prof"):
     ]
 
 
-_PRIMARY = ("tile_kernel", "gemm_kernel", "quant_kernel")
+_PRIMARY = ("tile_kernel", "walk_kernel", "gemm_kernel", "quant_kernel")
 _FOLLOWER = ("splitk_reduce_kernel", "tail_reduce_kernel")  # run right after their call's tile kernel
 
 
@@ -461,7 +461,7 @@ def summarize_profile(d, workload):
         r0 = grps[0][0]
         names = []
         for r in grps[0]:
-            m = re.search(r"(tile_kernel|gemm_kernel|tail_reduce_kernel)<[^>]*>|splitk_reduce_kernel|quant_kernel", r["Kernel_Name"])
+            m = re.search(r"(tile_kernel|walk_kernel|gemm_kernel|tail_reduce_kernel)<[^>]*>|splitk_reduce_kernel|quant_kernel", r["Kernel_Name"])
             names.append(m.group(0) if m else r["Kernel_Name"])
         name = " + ".join(names)
         grid = (int(r0["Grid_Size_X"]) // int(r0["Workgroup_Size_X"]), int(r0["Grid_Size_Y"]))
