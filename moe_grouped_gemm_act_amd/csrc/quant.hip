@@ -15,7 +15,10 @@
 // workgroup takes 64 rows of one K block; four threads share a row (32
 // elements, four 16-byte loads each) and meet in a two-step lane exchange
 // for the block maximum; the 64 scales of the block are one contiguous run
-// of sa.  (One wave per row with 1 KB row reads measured slower.)
+// of sa.  (One wave per row with 1 KB row reads measured slower.)  The grid
+// runs K blocks fastest, so the workgroups in flight read whole rows
+// together: 9-20% faster than row groups fastest at K = 16384, 18432 and
+// 1536 (8% slower at K = 7168).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,7 +42,7 @@ constexpr int QROWS = 64;  // rows per workgroup
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *X, uint8_t *A, float *sa,
                                                     int M, int K) {
   const int tid = threadIdx.x, row = tid >> 2, q = tid & 3;
-  const int kb = blockIdx.y, m = blockIdx.x * QROWS + row;
+  const int kb = blockIdx.x, m = blockIdx.y * QROWS + row;
   const bool live = m < M;
   // elements [kb*128 + q*32, +32) of row m: four 16-byte loads; rows past M
   // read out of range (zeros, no traffic)
@@ -89,7 +92,8 @@ extern "C" int quantize_fp8_1x128(const void *X, void *A, float *sa, int M, int 
   if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(A) % 16 ||
       reinterpret_cast<uintptr_t>(sa) % 4)
     return FP8GEMM_MISALIGNED;
-  hipLaunchKernelGGL(quant_kernel, dim3((M + QROWS - 1) / QROWS, K / 128), dim3(256), 0,
+  if ((M + QROWS - 1) / QROWS > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
+  hipLaunchKernelGGL(quant_kernel, dim3(K / 128, (M + QROWS - 1) / QROWS), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(X),
                      static_cast<uint8_t *>(A), sa, M, K);
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
