@@ -338,12 +338,15 @@ __device__ __forceinline__ int fresh_lane_id() {
 // 0..15 of the block tile; slot rows 0..BM-1 are activations, BM.. weights.
 
 // Product k = j * TN + i of a K block (activation group j, weight group i)
-// comes from one MFMA; it is promoted LAG MFMAs later, when it has long
+// comes from one MFMA; it is promoted lag MFMAs later, when it has long
 // landed, so the promotion FMAs issue in the shadow of the next MFMAs instead
-// of waiting on the one just issued.  Products sit in a ring of RING
-// registers; TN * TM is a multiple of RING, so slots and the promotion of the
-// previous block's last products line up across blocks.
-constexpr int LAG = 2, RING = 4;
+// of waiting on the one just issued.  Products sit in a ring of `ring`
+// registers; TN * TM is a multiple of it, so slots and the promotion of the
+// previous block's last products line up across blocks.  Lag 2 in a ring of
+// 4; tiles of two products per block (narrow decode tiles) use lag 1 in a
+// ring of 2.
+template <int TN, int TM>
+constexpr int ring_size() { return (TN * TM) % 4 == 0 ? 4 : 2; }
 
 // One FP8 K block from slot `sl` (activation scales after the operand rows),
 // with the wave's weight scale sbv: acc += (sa sb) (A_blk B_blk^T), the last
@@ -355,8 +358,9 @@ constexpr int LAG = 2, RING = 4;
 // once.
 template <int WGN, int TN, int TM, int BM>
 __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn, int wm, int fr,
-                                           int fg, v4f (&acc)[TN][TM], v4f (&ring)[RING],
-                                           float &sc_last) {
+                                           int fg, v4f (&acc)[TN][TM],
+                                           v4f (&ring)[ring_size<TN, TM>()], float &sc_last) {
+  constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
   constexpr int ROWS = BM + WGN * TN * 16;
   static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
   const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
@@ -402,9 +406,11 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn,
   sc_last = scb[TM - 1];
 }
 
-// the last block's last LAG products
+// the last block's last lag products
 template <int TN, int TM>
-__device__ __forceinline__ void fp8_flush(v4f (&acc)[TN][TM], const v4f (&ring)[RING], float sc_last) {
+__device__ __forceinline__ void fp8_flush(v4f (&acc)[TN][TM], const v4f (&ring)[ring_size<TN, TM>()],
+                                          float sc_last) {
+  constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
 #pragma unroll
   for (int k = TN * TM - LAG; k < TN * TM; ++k)
 #pragma unroll
@@ -499,7 +505,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   constexpr int MAXKB = 160;                // K <= 20480 for the weight-scale preload
   constexpr int NCW = WGN * WGM;            // compute waves
   constexpr int CT = NCW * 64;              // compute threads
-  static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 64 == 0 &&
+  static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 32 == 0 &&
                     128 % (TN * 16) == 0, "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
   // ACT (fused SwiGLU): the tile's weight rows are 128 gate rows (waves
@@ -686,9 +692,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
       s_sb[h][t] = sb[(size_t)blk * Kb + kb0 + t];
     }
     __builtin_amdgcn_s_waitcnt(0);
-    v4f ring[RING];
+    v4f ring[ring_size<TN, TM>()];
 #pragma unroll
-    for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < ring_size<TN, TM>(); ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
     float sc_last = 0.f;  // scale of the previous block's last activation group
     for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
@@ -1067,9 +1073,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
         cs = cs + 1 == STAGES ? 0 : cs + 1;
       }
     } else {
-      v4f ring[RING];
+      v4f ring[ring_size<TN, TM>()];
 #pragma unroll
-      for (int q = 0; q < RING; ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < ring_size<TN, TM>(); ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
       float sc_last = 0.f;
       for (int t = 0; t < it.nk; ++t) {
         asm volatile("" ::: "memory");
@@ -1234,7 +1240,7 @@ struct DecodeCfg {
 // slots for bn = 128, and for bn = 64 with 128 activation rows.
 bool decode_built(int bn, int stages, int bm, int waves) {
   if (waves == 8) return stages == 4 && (bn == 128 || (bn == 64 && bm == 128));
-  return waves == 4 && ((bn == 64 && (stages == 4 || stages == 6)) || (bn == 128 && stages == 4));
+  return waves == 4 && ((bn == 64 && (stages == 4 || stages == 6)) || ((bn == 128 || bn == 32) && stages == 4));
 }
 
 // Default (measured on MI355X over the decode shapes, weights streamed from
@@ -1254,6 +1260,14 @@ DecodeCfg decode_config(int M, int N, int Kb, bool bf) {
   DecodeCfg c{tiles64 >= 384 ? 128 : 64, 4, 1, 4};
   const int tiles = cdiv(N, c.bn) * cdiv(M, bm);
   c.splits = std::max(1, std::min(256 / std::max(tiles, 1), Kb / 9));
+  // K too short to split but half the CUs idle: 32-row weight tiles double
+  // the workgroups without partials (64 and 128 x 7168 x 2048: 8.5 -> 7.3 and
+  // 11.0 -> 9.4 us; each workgroup streams half the weights and the same
+  // activations)
+  if (c.splits == 1 && c.bn == 64 && 2 * tiles <= 256) {
+    c.bn = 32;
+    return c;
+  }
   // eight compute waves (two per SIMD, so one's promotion FMAs overlap the
   // other's MFMAs) where the tile has the rows for them and K is not split:
   // 2-4% on 24576x1536 and on 128x7168x2048, slower with a K split
@@ -1297,6 +1311,7 @@ int run_decode(Args a, hipStream_t stream) {
   DEC(64, 4)
   DEC(64, 6)
   DEC(128, 4)
+  DEC(32, 4)
 #undef DEC
   if (st != FP8GEMM_OK || a.splits == 1) return st;
   const long long quads = (long long)a.M * cdiv(a.N, 4);
