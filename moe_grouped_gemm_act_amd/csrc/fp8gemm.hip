@@ -349,23 +349,25 @@ template <int TN, int TM>
 constexpr int ring_size() { return (TN * TM) % 4 == 0 ? 4 : 2; }
 
 // One FP8 K block from slot `sl` (activation scales after the operand rows),
-// with the wave's weight scale sbv: acc += (sa sb) (A_blk B_blk^T), the last
+// with the wave's weight scale sbv (SPLITB: sbv for fragments i < TN / 2 and
+// sbv_hi for the rest, which come from another 128-row weight block):
+// acc += (sa sb) (A_blk B_blk^T), the last
 // LAG products carried to the next block (or fp8_flush).  The next activation
 // fragment and its scale are read from LDS one group ahead.  Large tiles
 // (WGN > 1) read only their first two weight fragments before the first MFMA
 // and the rest one MFMA ahead of use, so the compute waves, released together
 // by the barrier, do not all queue their whole fragment reads on the LDS at
 // once.
-template <int WGN, int TN, int TM, int BM>
-__device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn, int wm, int fr,
-                                           int fg, v4f (&acc)[TN][TM],
-                                           v4f (&ring)[ring_size<TN, TM>()], float &sc_last) {
+template <int WGN, int TN, int TM, int BM, bool SPLITB = false>
+__device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float sbv_hi, int wn, int wm,
+                                           int fr, int fg, v4f (&acc)[TN][TM],
+                                           v4f (&ring)[ring_size<TN, TM>()], float (&sc_last)[2]) {
   constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
   constexpr int ROWS = BM + WGN * TN * 16;
   static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
   const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
   v8i bfr[TN], afr[2];
-  float scb[TM];
+  float scb[TM], sch[TM];  // activation scale times the weight scale of fragments i < TN / 2, and the rest
   constexpr int B0 = WGN > 1 && TN > 2 ? 2 : TN;
 #pragma unroll
   for (int i = 0; i < B0; ++i) {
@@ -376,6 +378,7 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn,
     const int row = wm * TM * 16 + fr;
     afr[0] = frag(sl + row * BK, row, fg);
     scb[0] = ssl[row] * sbv;
+    sch[0] = SPLITB ? ssl[row] * sbv_hi : scb[0];
   }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
@@ -383,6 +386,7 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn,
       const int row = (wm * TM + j + 1) * 16 + fr;
       afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
       scb[j + 1] = ssl[row] * sbv;
+      sch[j + 1] = SPLITB ? ssl[row] * sbv_hi : scb[j + 1];
     }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
@@ -396,26 +400,87 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, int wn,
           bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
       const int kp = k - LAG;                      // product promoted now
       const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
-      const float sp = kp >= 0 ? scb[kq / TN] : sc_last;
+      const bool hi = SPLITB && kq % TN >= TN / 2;
+      const float sp = kp >= 0 ? (hi ? sch[kq / TN] : scb[kq / TN]) : sc_last[hi ? 1 : 0];
       v4f &ap = acc[kq % TN][kq / TN];
       const v4f &pp = ring[(kq + RING) % RING];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ap[r] = __builtin_fmaf(pp[r], sp, ap[r]);
     }
   }
-  sc_last = scb[TM - 1];
+  sc_last[0] = scb[TM - 1];
+  sc_last[1] = sch[TM - 1];
 }
 
 // the last block's last lag products
-template <int TN, int TM>
+template <int TN, int TM, bool SPLITB = false>
 __device__ __forceinline__ void fp8_flush(v4f (&acc)[TN][TM], const v4f (&ring)[ring_size<TN, TM>()],
-                                          float sc_last) {
+                                          const float (&sc_last)[2]) {
   constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
 #pragma unroll
-  for (int k = TN * TM - LAG; k < TN * TM; ++k)
+  for (int k = TN * TM - LAG; k < TN * TM; ++k) {
+    const float sp = sc_last[SPLITB && k % TN >= TN / 2 ? 1 : 0];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sc_last, acc[k % TN][k / TN][r]);
+      acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sp, acc[k % TN][k / TN][r]);
+  }
+}
+
+// SwiGLU weight tiles (256 rows for 128 outputs of y = silu(g) u): row rw of
+// the tile is gate row (rw < 32 within each 64-row group) or the matching up
+// row, so a compute wave's fragments i < 2 hold gate values and i + 2 the up
+// values of the same 32 outputs, in the same lanes.  Weight row in B of tile
+// row rw, for output tile tn of I = N / 2 outputs.
+__device__ __forceinline__ int swiglu_row(int rw, int tn, int I) {
+  return ((rw & 32) ? I : 0) + tn * 128 + (rw >> 6) * 32 + (rw & 31);
+}
+
+// SwiGLU epilogue of one compute wave (wn, wm) of a 256 x BM tile: y for its
+// 32 outputs in registers, the rows' maxima over the tile's 128 outputs
+// through s_rmax (4 x BM floats; one workgroup barrier, which every wave of
+// the workgroup, loaders included, must take at the same point), then the
+// e4m3 codes of y / s with s = amax|y| / 448 for each row and its scale.
+// Rows: m < mvalid (CONTIG: rows whose index names expert g).
+template <int TM, int BM, int LAYOUT>
+__device__ __forceinline__ void swiglu_epilogue(v4f (&acc)[4][TM], float *s_rmax, uint8_t *act,
+                                                float *act_scale, const int32_t *idx, int g, int M,
+                                                int I, int mvalid, int m0, int tn, int wn, int wm) {
+  const int lid = fresh_lane_id();
+  const int fr = lid & 15, fg = lid >> 4;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gv = acc[i][j][r];
+        // silu(g) = g / (1 + e^-g): hardware exponential and reciprocal
+        acc[i][j][r] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * acc[i + 2][j][r];
+        mx = fmaxf(mx, fabsf(acc[i][j][r]));  // NaN is skipped, as in the quantiser
+      }
+    // the row's other values of this wave sit in lanes fr + 16, + 32, + 48
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (fg == 0) s_rmax[wn * BM + (wm * TM + j) * 16 + fr] = mx;
+  }
+  __syncthreads();  // every wave's row maxima
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int ml = (wm * TM + j) * 16 + fr, m = m0 + ml;
+    const float amax = fmaxf(fmaxf(s_rmax[ml], s_rmax[BM + ml]), fmaxf(s_rmax[2 * BM + ml], s_rmax[3 * BM + ml]));
+    const float sc = amax == 0.f ? 1.f : amax / 448.f;
+    const E4m3Quotient qd(amax, sc);
+    bool ok = m < mvalid;
+    if (LAYOUT == CONTIG) ok = m < M && idx[m] == g;
+    if (!ok) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint32_t *>(act + (size_t)m * I + tn * 128 + wn * 32 + i * 16 + 4 * fg) =
+          e4m3_pack4(qd.quotient(acc[i][j][0]), qd.quotient(acc[i][j][1]), qd.quotient(acc[i][j][2]),
+                     qd.quotient(acc[i][j][3]), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    if (wn == 0 && fg == 0) act_scale[(size_t)tn * M + m] = sc;
+  }
 }
 
 // One BF16 K block (64 elements, 128 bytes a row).  No scales, so products
@@ -508,13 +573,14 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 32 == 0 &&
                     128 % (TN * 16) == 0, "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
-  // ACT (fused SwiGLU): the tile's weight rows are 128 gate rows (waves
-  // wn < WGN/2) and the 128 matching up rows; its output is 128 columns of y
+  // ACT (fused SwiGLU): the tile's 256 weight rows are 128 gate rows and the
+  // 128 matching up rows, interleaved 32 by 32 (swiglu_row); its output is
+  // 128 columns of y
   static_assert(!ACT || (BN == 256 && WGN == 4 && TN == 4 && BM <= 128), "SwiGLU tile shape");
   static_assert(!(ACT && BF), "the fused SwiGLU takes FP8 operands");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ float s_sb[BN > 128 ? 2 : 1][BF ? 1 : MAXKB];
-  __shared__ float s_rmax[ACT ? 2 : 1][ACT ? BM : 1];  // ACT: row maxima of y per gate wave column
+  __shared__ float s_rmax[ACT ? 4 * BM : 1];  // ACT: row maxima of y per wave column
   __shared__ int s_group;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -611,8 +677,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         off[q] = m0 + r < mvalid ? (uint32_t)(m0 + r) * RB + col * 16 : OOB;
       } else {
         const int rw = r - BM;  // weight row of the tile
-        // ACT: gate rows 128 tn + rw, then up rows N/2 + 128 tn + (rw - 128)
-        const int grow = ACT ? (rw < 128 ? tn * 128 + rw : N / 2 + tn * 128 + rw - 128) : n0 + rw;
+        const int grow = ACT ? swiglu_row(rw, tn, N / 2) : n0 + rw;
         off[q] = grow < N ? (uint32_t)grow * RB + col * 16 : OOB;
       }
     }
@@ -653,19 +718,14 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     }
 #undef TK_G
     __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
-    if (ACT) {                      // the three barriers of the SwiGLU epilogue
-      __syncthreads();
-      __syncthreads();
-      __syncthreads();
-    }
+    if (ACT) __syncthreads();  // the SwiGLU epilogue's barrier
     return;
   }
 
   // ---------------- compute waves ----------------
-  // ACT: waves 0-3 take the gate columns (wn < 2), one per SIMD, so the
-  // epilogue's arithmetic, which only they do, is spread over the four SIMDs
-  const int wn = ACT ? wave >> 1 : wave % WGN, wm = ACT ? wave & 1 : wave / WGN;
-  const int hsb = (wn * TN * 16) / 128;  // which weight-scale block this wave's rows use
+  const int wn = wave % WGN, wm = wave / WGN;
+  // which weight-scale block this wave's rows use (ACT: gate block 0, up block 1)
+  const int hsb = ACT ? 0 : (wn * TN * 16) / 128;
   v4f acc[TN][TM];
 #pragma unroll
   for (int i = 0; i < TN; ++i)
@@ -695,7 +755,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
     v4f ring[ring_size<TN, TM>()];
 #pragma unroll
     for (int q = 0; q < ring_size<TN, TM>(); ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    float sc_last = 0.f;  // scale of the previous block's last activation group
+    float sc_last[2] = {0.f, 0.f};  // scales of the previous block's last activation group
     for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
       for (int u = 0; u < STAGES; ++u) {
@@ -709,77 +769,17 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         // addresses in registers through the loop
         int so = u * SLOT;
         if (ACT) asm volatile("" : "+s"(so));
-        fp8_kblock<WGN, TN, TM, BM>(&lds[0][0] + so, s_sb[hsb][t], wn, wm, fr, fg, acc, ring, sc_last);
+        fp8_kblock<WGN, TN, TM, BM, ACT>(&lds[0][0] + so, s_sb[hsb][t], s_sb[ACT ? 1 : hsb][t], wn, wm,
+                                         fr, fg, acc, ring, sc_last);
       }
     }
-    fp8_flush(acc, ring, sc_last);
+    fp8_flush<TN, TM, ACT>(acc, ring, sc_last);
   }
 
   if constexpr (ACT) {
-    // Fused SwiGLU and 1x128 requantisation of y = silu(g) u.  Gate values sit
-    // in waves wn < 2 and the matching up values in waves wn + 2 (same lanes);
-    // the up values cross over through the LDS ring, free once every wave is
-    // past the K loop.  A row's 128 outputs are held by the two gate waves of
-    // its activation group: their maxima meet in LDS, and both then encode
-    // their half with the block scale s = amax|y| / 448.
-    constexpr int UPS = 132;  // floats per exchange row (16-byte aligned rows)
-    static_assert(BM * UPS * 4 <= STAGES * SLOT, "up-value exchange fits the ring");
-    float *up = reinterpret_cast<float *>(&lds[0][0]);
-    const int I = N / 2;
-    const int lid = fresh_lane_id();
-    const int fr = lid & 15, fg = lid >> 4;
-    __syncthreads();  // (1) the loaders have drained: the ring may be reused
-    if (wn >= 2) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-#pragma unroll
-        for (int i = 0; i < TN; ++i)
-          *reinterpret_cast<v4f *>(up + ((wm * TM + j) * 16 + fr) * UPS + (wn - 2) * 64 + i * 16 +
-                                   4 * fg) = acc[i][j];
-    }
-    __syncthreads();  // (2) up values in LDS
-    if (wn < 2) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        float mx = 0.f;
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const v4f u4 = *reinterpret_cast<const v4f *>(
-              up + ((wm * TM + j) * 16 + fr) * UPS + wn * 64 + i * 16 + 4 * fg);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gv = acc[i][j][r];
-            // silu(g) = g / (1 + e^-g): hardware exponential and reciprocal
-            acc[i][j][r] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * u4[r];
-            mx = fmaxf(mx, fabsf(acc[i][j][r]));  // NaN is skipped, as in the quantiser
-          }
-        }
-        // the row's other 48 values of this wave sit in lanes fr + 16, + 32, + 48
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (fg == 0) s_rmax[wn][(wm * TM + j) * 16 + fr] = mx;
-      }
-    }
-    __syncthreads();  // (3) row maxima of both gate waves
-    if (wn < 2) {
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int ml = (wm * TM + j) * 16 + fr, m = m0 + ml;
-        const float amax = fmaxf(s_rmax[0][ml], s_rmax[1][ml]);
-        const float sc = amax == 0.f ? 1.f : amax / 448.f;
-        const E4m3Quotient qd(amax, sc);
-        bool ok = m < mvalid;
-        if (LAYOUT == CONTIG) ok = m < M && a.idx[m] == g;
-        if (!ok) continue;
-#pragma unroll
-        for (int i = 0; i < TN; ++i)
-          *reinterpret_cast<uint32_t *>(act + (size_t)m * I + tn * 128 + wn * 64 + i * 16 + 4 * fg) =
-              e4m3_pack4(qd.quotient(acc[i][j][0]), qd.quotient(acc[i][j][1]),
-                         qd.quotient(acc[i][j][2]), qd.quotient(acc[i][j][3]), acc[i][j][0],
-                         acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (wn == 0 && fg == 0) act_scale[(size_t)tn * M + m] = sc;
-      }
-    }
+    // fused SwiGLU and 1x128 requantisation of y = silu(g) u
+    swiglu_epilogue<TM, BM, LAYOUT>(acc, s_rmax, act, act_scale, a.idx, g, M, N / 2, mvalid, m0, tn,
+                                    wn, wm);
     return;
   }
 
@@ -834,7 +834,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
 constexpr int WALK_MAXIT = 256;  // items per workgroup, at most (contiguous)
 constexpr int WALK_MAXG = 512;   // experts, at most (masked)
 
-template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF>
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF, bool ACT = false>
 __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   constexpr int ROWS = BM + BN;
@@ -851,8 +851,10 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
                 "tile shape");
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
   static_assert(LAYOUT != CONTIG || BM <= 128, "one expert per activation tile");
+  static_assert(!ACT || (BN == 256 && WGN == 4 && TN == 4 && BM <= 128 && !BF), "SwiGLU tile shape");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ int s_grp[LAYOUT == CONTIG ? WALK_MAXIT : 1];
+  __shared__ float s_rmax[ACT ? 4 * BM : 1];  // ACT: row maxima of y per wave column
   // masked: items before expert g's (s_pre[g]) and its valid rows (s_mv[g])
   __shared__ int s_pre[LAYOUT == MASKED ? WALK_MAXG + 1 : 1];
   __shared__ int s_mv[LAYOUT == MASKED ? WALK_MAXG : 1];
@@ -996,7 +998,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
         for (int q = 0; q < DMA; ++q) {
           const int r = (L + NLD * q) * 8 + (lane >> 3);
           const int col = (lane & 7) ^ row_key(r);
-          const int grow = q < QA ? it.m0 + r : it.n0 + r - BM;
+          const int grow = q < QA ? it.m0 + r : ACT ? swiglu_row(r - BM, it.n0 / BN, N / 2) : it.n0 + r - BM;
           off[q] = grow < (q < QA ? it.mvalid : N) ? (uint32_t)grow * RB + col * 16 : OOB;
         }
         if (!BF) {
@@ -1005,8 +1007,10 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
             const int m = it.m0 + ((L + NLD * jj) % SG) * 64 + lane;
             soff[jj] = m < it.mvalid ? (uint32_t)m * 4 : OOB;
           }
-          // lane h < BN / 128: the scale row of the tile's h-th 128-row weight block
-          sboff = lane < BN / 128 ? (uint32_t)min(it.n0 / 128 + lane, Nb - 1) * Kb * 4 : OOB;
+          // lane h < BN / 128: the scale row of the tile's h-th 128-row weight
+          // block (ACT: the gate block, then the up block)
+          const int blk = ACT ? (lane == 0 ? it.n0 / BN : N / 256 + it.n0 / BN) : min(it.n0 / 128 + lane, Nb - 1);
+          sboff = lane < BN / 128 ? (uint32_t)blk * Kb * 4 : OOB;
         }
         pkb0 = it.kb0;
         pnk = it.nk;
@@ -1045,6 +1049,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
         produce(ps);
         ps = ps + 1 == STAGES ? 0 : ps + 1;
       }
+      // ACT: the SwiGLU epilogue's barrier; the next item's first blocks are
+      // already in flight
+      if (ACT) __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_s_waitcnt(0);  // nothing may still write LDS when the workgroup ends
     return;
@@ -1053,7 +1060,8 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
   // ---------------- compute waves ----------------
   const int lane = tid & 63, fr = lane & 15, fg = lane >> 4;
   const int wn = wave % WGN, wm = wave / WGN;
-  const int hsb = (wn * TN * 16) / 128;  // which of the slot's weight scales this wave's rows use
+  // which of the slot's weight scales this wave's rows use (ACT: gate 0, up 1)
+  const int hsb = ACT ? 0 : (wn * TN * 16) / 128;
   int cs = 0;                            // slot of the next block
   for (int k = 0; k < nit; ++k) {
     if (group(k) < 0) continue;  // all padding: nothing loaded, nothing written
@@ -1076,19 +1084,26 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
       v4f ring[ring_size<TN, TM>()];
 #pragma unroll
       for (int q = 0; q < ring_size<TN, TM>(); ++q) ring[q] = v4f{0.f, 0.f, 0.f, 0.f};
-      float sc_last = 0.f;
+      float sc_last[2] = {0.f, 0.f};
       for (int t = 0; t < it.nk; ++t) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // this item's block t is in slot cs
         asm volatile("" ::: "memory");
         const uint8_t *sl = &lds[0][0] + cs * SLOT;
-        const float sbv = reinterpret_cast<const float *>(sl + SBOFF)[hsb];
-        fp8_kblock<WGN, TN, TM, BM>(sl, sbv, wn, wm, fr, fg, acc, ring, sc_last);
+        const float *sbs = reinterpret_cast<const float *>(sl + SBOFF);
+        fp8_kblock<WGN, TN, TM, BM, ACT>(sl, sbs[hsb], sbs[ACT ? 1 : hsb], wn, wm, fr, fg, acc, ring,
+                                         sc_last);
         cs = cs + 1 == STAGES ? 0 : cs + 1;
       }
-      fp8_flush(acc, ring, sc_last);
+      fp8_flush<TN, TM, ACT>(acc, ring, sc_last);
     }
-    if (it.tail) {
+    if constexpr (ACT) {
+      const int I = N / 2;
+      swiglu_epilogue<TM, BM, LAYOUT>(
+          acc, s_rmax, a.act + (LAYOUT == MASKED ? (size_t)g * M * I : 0),
+          a.act_scale + (LAYOUT == MASKED ? (size_t)g * (N / 256) * M : 0), a.idx, g, M, I,
+          it.mvalid, it.m0, it.n0 / BN, wn, wm);
+    } else if (it.tail) {
       store_part<TN, TM, BN>(acc, a.ws + ((size_t)(it.tile - F) * a.tail_splits + it.split) * (BM * BN),
                              wn, wm, fr, fg);
     } else {
@@ -1351,10 +1366,11 @@ int walk_workgroups() {
 // tile: 9% faster at FP8 K = 1536, 2-4% on the contiguous K = 7168 calls,
 // 2-3% slower at K = 16384 and 18432, where a tile's fixed costs are a small
 // share of its time and the walk's runtime slot indexing costs a little in
-// every block.  Masked calls keep one workgroup per (tile, expert) unless
-// FP8GEMM_WALK=2: their walk over the live tiles measured the same per call
-// and up to 3% slower over the two masked workload calls.  FP8GEMM_WALK=0
-// turns the walk off everywhere (tuning overrides).
+// every block.  Plain masked calls keep one workgroup per (tile, expert)
+// unless FP8GEMM_WALK=2: their walk over the live tiles measured the same per
+// call and up to 3% slower over the two masked workload calls (the masked
+// SwiGLU call walks by default).  FP8GEMM_WALK=0 turns the walk off
+// everywhere (tuning overrides).
 bool walk_enabled(int row_bytes, bool masked = false) {
   const char *e = getenv("FP8GEMM_WALK");
   if (e && e[0] == '0') return false;
@@ -1362,12 +1378,12 @@ bool walk_enabled(int row_bytes, bool masked = false) {
   return row_bytes <= 8192;
 }
 
-// a.tiles_m / tiles_n and the tail fields set; `items` work items in all
-template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF>
+// a.tiles_m / tiles_n and the tail fields set; P workgroups
+template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool BF, bool ACT = false>
 hipError_t launch_walk(Args &a, int P, hipStream_t stream) {
   void *kargs[] = {&a};
   return hipLaunchKernel(
-      reinterpret_cast<const void *>(&walk_kernel<WGN, WGM, TN, TM, STAGES, NLD, LAYOUT, BF>),
+      reinterpret_cast<const void *>(&walk_kernel<WGN, WGM, TN, TM, STAGES, NLD, LAYOUT, BF, ACT>),
       dim3(P), dim3((WGN * WGM + NLD) * 64), kargs, 0, stream);
 }
 
@@ -1558,7 +1574,16 @@ int grouped_contiguous_swiglu_fp8(const void *A, const float *sa, const void *B,
   if (M % 128 != 0) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb, nullptr, M,
          2 * I, K, G, m_indices, 0, 0, 1, K / BK, nullptr, static_cast<uint8_t *>(Y), sy};
-  return launch_tile<4, 2, 4, 4, 3, 4, CONTIG, false, true>(a, 1, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the persistent walk as for the plain contiguous call
+  const int P = walk_workgroups();
+  const int T = (M / 128) * (I / 128);
+  if (!walk_enabled(K) || P < 8 || T <= P || cdiv(T, P) > WALK_MAXIT)
+    return launch_tile<4, 2, 4, 4, 3, 4, CONTIG, false, true>(a, 1, s);
+  a.tiles_m = M / 128;
+  a.tiles_n = I / 128;
+  return launch_walk<4, 2, 4, 4, 3, 4, CONTIG, false, true>(a, P, s) == hipSuccess ? FP8GEMM_OK
+                                                                                  : FP8GEMM_LAUNCH_FAILED;
 }
 
 int grouped_masked_swiglu_fp8(const void *A, const float *sa, const void *B, const float *sb,
@@ -1571,7 +1596,16 @@ int grouped_masked_swiglu_fp8(const void *A, const float *sa, const void *B, con
   if (G > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb, nullptr, M,
          2 * I, K, G, masked_m, 0, 0, 1, K / BK, nullptr, static_cast<uint8_t *>(Y), sy};
-  return launch_tile<4, 2, 4, 4, 3, 4, MASKED, false, true>(a, G, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the walk over the live tiles: 13% faster than one workgroup per (tile,
+  // expert) here (the plain masked call measured level)
+  const int P = walk_workgroups();
+  if (!walk_enabled(K) || P < 8 || G > WALK_MAXG)
+    return launch_tile<4, 2, 4, 4, 3, 4, MASKED, false, true>(a, G, s);
+  a.tiles_m = cdiv(M, 128);
+  a.tiles_n = I / 128;
+  return launch_walk<4, 2, 4, 4, 3, 4, MASKED, false, true>(a, P, s) == hipSuccess ? FP8GEMM_OK
+                                                                                  : FP8GEMM_LAUNCH_FAILED;
 }
 
 // BF16 GEMM without scales: shared checks (sizes in elements; bytes are twice)
