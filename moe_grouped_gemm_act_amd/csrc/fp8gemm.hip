@@ -831,6 +831,10 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
 // live tiles, expert by expert (ceil(masked_m[g] / BM) activation tiles by
 // the weight tiles); every workgroup builds the experts' offsets into it from
 // masked_m on the device, and finds an item's expert by binary search.
+// ACT (fused SwiGLU, 256 x 128 tiles of interleaved gate/up rows): after a
+// tile's last block every wave, loaders included, takes one more barrier
+// for the epilogue's row maxima (swiglu_epilogue); the LDS ring is not used
+// by the epilogue, so the prefetch of the next tile goes on.
 constexpr int WALK_MAXIT = 256;  // items per workgroup, at most (contiguous)
 constexpr int WALK_MAXG = 512;   // experts, at most (masked)
 
