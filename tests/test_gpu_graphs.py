@@ -148,3 +148,27 @@ def test_two_streams_split_k_concurrently():
     for D, r in zip(outs, ref):
         assert (bits(D) == r).all()
     announce("two streams: split-K results equal the serial ones")
+
+
+def test_graph_persistent_walk_calls():
+    """The persistent walk under capture: a dense call with a tail split
+    (workspace made by the eager call before capture), a contiguous call and
+    a contiguous SwiGLU call, each with more tiles than CUs."""
+    d = W.dense(8870, 1100, 7400, 2048)  # 261 tiles: 256 whole + 5 split in 4
+    A, sa, B, sb = (to_gpu(d[k]) for k in ("A", "sa", "B", "sb"))
+    D = torch.empty((1100, 7400), dtype=torch.bfloat16, device="cuda")
+    replay_equals_eager("walk dense 1100x7400x2048", lambda: fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D), [D])
+    c = W.contiguous(8871, 5, 128 * 20, 4352, 256, uniform=False)  # 20 x 17 tiles
+    cA, csa, cB, csb, cidx = (to_gpu(c[k]) for k in ("A", "sa", "B", "sb", "m_indices"))
+    Dc = torch.empty((c["M"], c["N"]), dtype=torch.bfloat16, device="cuda")
+    replay_equals_eager("walk contiguous 2560x4352x256",
+                        lambda: fg.grouped_contiguous(cA, csa, cB, csb, cidx, Dc), [Dc])
+    G, rows, I, K = 4, 128 * 20, 2048, 256  # 20 x 16 tiles
+    idx, _ = synth.contiguous_indices(8873, G, rows, False)
+    sA, ssa = synth.act(8874, rows, K)
+    sB, ssb = synth.grouped_weight(8875, G, 2 * I, K)
+    tA, tsa, tB, tsb, tidx = to_gpu(sA), to_gpu(ssa), to_gpu(sB), to_gpu(ssb), to_gpu(idx)
+    Y = torch.empty((rows, I), dtype=torch.uint8, device="cuda")
+    sy = torch.empty((I // 128, rows), dtype=torch.float32, device="cuda")
+    replay_equals_eager("walk contiguous swiglu 2560x4096x256",
+                        lambda: fg.grouped_contiguous_swiglu_fp8(tA, tsa, tB, tsb, tidx, Y, sy), [Y, sy])
