@@ -349,25 +349,25 @@ template <int TN, int TM>
 constexpr int ring_size() { return (TN * TM) % 4 == 0 ? 4 : 2; }
 
 // One FP8 K block from slot `sl` (activation scales after the operand rows),
-// with the wave's weight scale sbv (SPLITB: sbv for fragments i < TN / 2 and
-// sbv_hi for the rest, which come from another 128-row weight block):
-// acc += (sa sb) (A_blk B_blk^T), the last
+// with the wave's weight scale sbv (TWOB: fragment i takes sbv_hi instead
+// when bit i of himask is set, its rows lying in the next 128-row weight
+// block): acc += (sa sb) (A_blk B_blk^T), the last
 // LAG products carried to the next block (or fp8_flush).  The next activation
 // fragment and its scale are read from LDS one group ahead.  Large tiles
 // (WGN > 1) read only their first two weight fragments before the first MFMA
 // and the rest one MFMA ahead of use, so the compute waves, released together
 // by the barrier, do not all queue their whole fragment reads on the LDS at
 // once.
-template <int WGN, int TN, int TM, int BM, bool SPLITB = false>
-__device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float sbv_hi, int wn, int wm,
-                                           int fr, int fg, v4f (&acc)[TN][TM],
+template <int WGN, int TN, int TM, int BM, bool TWOB = false>
+__device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float sbv_hi, unsigned himask,
+                                           int wn, int wm, int fr, int fg, v4f (&acc)[TN][TM],
                                            v4f (&ring)[ring_size<TN, TM>()], float (&sc_last)[2]) {
   constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
   constexpr int ROWS = BM + WGN * TN * 16;
   static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
   const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
   v8i bfr[TN], afr[2];
-  float scb[TM], sch[TM];  // activation scale times the weight scale of fragments i < TN / 2, and the rest
+  float scb[TM], sch[TM];  // activation scale times the weight scale sbv, and times sbv_hi
   constexpr int B0 = WGN > 1 && TN > 2 ? 2 : TN;
 #pragma unroll
   for (int i = 0; i < B0; ++i) {
@@ -378,7 +378,7 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float s
     const int row = wm * TM * 16 + fr;
     afr[0] = frag(sl + row * BK, row, fg);
     scb[0] = ssl[row] * sbv;
-    sch[0] = SPLITB ? ssl[row] * sbv_hi : scb[0];
+    sch[0] = TWOB ? ssl[row] * sbv_hi : scb[0];
   }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
@@ -386,7 +386,7 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float s
       const int row = (wm * TM + j + 1) * 16 + fr;
       afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
       scb[j + 1] = ssl[row] * sbv;
-      sch[j + 1] = SPLITB ? ssl[row] * sbv_hi : scb[j + 1];
+      sch[j + 1] = TWOB ? ssl[row] * sbv_hi : scb[j + 1];
     }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
@@ -400,7 +400,7 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float s
           bfr[i], afr[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
       const int kp = k - LAG;                      // product promoted now
       const int kq = kp >= 0 ? kp : kp + TN * TM;  // its index in its own block
-      const bool hi = SPLITB && kq % TN >= TN / 2;
+      const bool hi = TWOB && ((himask >> (kq % TN)) & 1u);
       const float sp = kp >= 0 ? (hi ? sch[kq / TN] : scb[kq / TN]) : sc_last[hi ? 1 : 0];
       v4f &ap = acc[kq % TN][kq / TN];
       const v4f &pp = ring[(kq + RING) % RING];
@@ -413,13 +413,13 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float s
 }
 
 // the last block's last lag products
-template <int TN, int TM, bool SPLITB = false>
+template <int TN, int TM, bool TWOB = false>
 __device__ __forceinline__ void fp8_flush(v4f (&acc)[TN][TM], const v4f (&ring)[ring_size<TN, TM>()],
-                                          const float (&sc_last)[2]) {
+                                          const float (&sc_last)[2], unsigned himask) {
   constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
 #pragma unroll
   for (int k = TN * TM - LAG; k < TN * TM; ++k) {
-    const float sp = sc_last[SPLITB && k % TN >= TN / 2 ? 1 : 0];
+    const float sp = sc_last[TWOB && ((himask >> (k % TN)) & 1u) ? 1 : 0];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       acc[k % TN][k / TN][r] = __builtin_fmaf(ring[k % RING][r], sp, acc[k % TN][k / TN][r]);
@@ -570,8 +570,12 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   constexpr int MAXKB = 160;                // K <= 20480 for the weight-scale preload
   constexpr int NCW = WGN * WGM;            // compute waves
   constexpr int CT = NCW * 64;              // compute threads
+  // a wave's weight rows lie in one 128-row scale block, or (TWOB: one wave
+  // column of 96 rows) in at most two
   static_assert((NCW == 4 || NCW == 8) && OCT % NLD == 0 && BM % 64 == 0 && BN % 32 == 0 &&
-                    128 % (TN * 16) == 0, "tile shape");
+                    (128 % (TN * 16) == 0 || (WGN == 1 && BN == 96)),
+                "tile shape");
+  constexpr bool TWOB = ACT || BN % 128 == 96;  // a wave reads two weight-scale blocks
   static_assert(PER_G * (STAGES - 1) < 64, "loads in flight per loader must fit vmcnt");
   // ACT (fused SwiGLU): the tile's 256 weight rows are 128 gate rows and the
   // 128 matching up rows, interleaved 32 by 32 (swiglu_row); its output is
@@ -579,7 +583,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   static_assert(!ACT || (BN == 256 && WGN == 4 && TN == 4 && BM <= 128), "SwiGLU tile shape");
   static_assert(!(ACT && BF), "the fused SwiGLU takes FP8 operands");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
-  __shared__ float s_sb[BN > 128 ? 2 : 1][BF ? 1 : MAXKB];
+  __shared__ float s_sb[BN > 128 || TWOB ? 2 : 1][BF ? 1 : MAXKB];
   __shared__ float s_rmax[ACT ? 4 * BM : 1];  // ACT: row maxima of y per wave column
   __shared__ int s_group;
 
@@ -726,6 +730,15 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   const int wn = wave % WGN, wm = wave / WGN;
   // which weight-scale block this wave's rows use (ACT: gate block 0, up block 1)
   const int hsb = ACT ? 0 : (wn * TN * 16) / 128;
+  // TWOB: the fragments whose rows use the second block (ACT: the up
+  // fragments 2 and 3; 96-row tiles: rows past the tile's first 128-row
+  // boundary)
+  unsigned himask = ACT ? 0xCu : 0u;
+  if (!ACT && TWOB) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      if ((n0 & 127) + i * 16 >= 128) himask |= 1u << i;
+  }
   v4f acc[TN][TM];
 #pragma unroll
   for (int i = 0; i < TN; ++i)
@@ -746,7 +759,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   } else {
     // the weight scales of the K range go to LDS while the loaders start; the
     // first K-block barrier publishes them
-    for (int i = tid; i < (BN > 128 ? 2 : 1) * nk; i += CT) {
+    for (int i = tid; i < (BN > 128 || TWOB ? 2 : 1) * nk; i += CT) {
       const int h = i / nk, t = i % nk;
       const int blk = ACT ? (h == 0 ? tn : N / 256 + tn) : min(n0 / 128 + h, Nb - 1);
       s_sb[h][t] = sb[(size_t)blk * Kb + kb0 + t];
@@ -769,11 +782,11 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         // addresses in registers through the loop
         int so = u * SLOT;
         if (ACT) asm volatile("" : "+s"(so));
-        fp8_kblock<WGN, TN, TM, BM, ACT>(&lds[0][0] + so, s_sb[hsb][t], s_sb[ACT ? 1 : hsb][t], wn, wm,
-                                         fr, fg, acc, ring, sc_last);
+        fp8_kblock<WGN, TN, TM, BM, TWOB>(&lds[0][0] + so, s_sb[hsb][t], s_sb[TWOB ? 1 : hsb][t],
+                                          himask, wn, wm, fr, fg, acc, ring, sc_last);
       }
     }
-    fp8_flush<TN, TM, ACT>(acc, ring, sc_last);
+    fp8_flush<TN, TM, TWOB>(acc, ring, sc_last, himask);
   }
 
   if constexpr (ACT) {
@@ -1095,11 +1108,11 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
         asm volatile("" ::: "memory");
         const uint8_t *sl = &lds[0][0] + cs * SLOT;
         const float *sbs = reinterpret_cast<const float *>(sl + SBOFF);
-        fp8_kblock<WGN, TN, TM, BM, ACT>(sl, sbs[hsb], sbs[ACT ? 1 : hsb], wn, wm, fr, fg, acc, ring,
-                                         sc_last);
+        fp8_kblock<WGN, TN, TM, BM, ACT>(sl, sbs[hsb], sbs[ACT ? 1 : hsb], ACT ? 0xCu : 0u, wn, wm, fr,
+                                         fg, acc, ring, sc_last);
         cs = cs + 1 == STAGES ? 0 : cs + 1;
       }
-      fp8_flush<TN, TM, ACT>(acc, ring, sc_last);
+      fp8_flush<TN, TM, ACT>(acc, ring, sc_last, ACT ? 0xCu : 0u);
     }
     if constexpr (ACT) {
       const int I = N / 2;
@@ -1255,11 +1268,13 @@ struct DecodeCfg {
 };
 
 // Instances built: four compute waves with (bn, stages) in {(64,4), (64,6),
-// (128,4)} for both activation tile heights; eight compute waves with four
-// slots for bn = 128, and for bn = 64 with 128 activation rows.
+// (128,4), (96,4), (32,4)} for both activation tile heights; eight compute
+// waves with four slots for bn = 128, and for bn = 64 with 128 activation
+// rows.
 bool decode_built(int bn, int stages, int bm, int waves) {
   if (waves == 8) return stages == 4 && (bn == 128 || (bn == 64 && bm == 128));
-  return waves == 4 && ((bn == 64 && (stages == 4 || stages == 6)) || ((bn == 128 || bn == 32) && stages == 4));
+  return waves == 4 &&
+         ((bn == 64 && (stages == 4 || stages == 6)) || ((bn == 128 || bn == 96 || bn == 32) && stages == 4));
 }
 
 // Default (measured on MI355X over the decode shapes, weights streamed from
@@ -1285,6 +1300,13 @@ DecodeCfg decode_config(int M, int N, int Kb, bool bf) {
   // activations)
   if (c.splits == 1 && c.bn == 64 && 2 * tiles <= 256) {
     c.bn = 32;
+    return c;
+  }
+  // no K split and 96-row tiles fill more of the chip in one wave (N = 24576:
+  // 256 tiles instead of 192 of 128 rows)
+  const int tiles96 = cdiv(N, 96) * cdiv(M, bm);
+  if (c.splits == 1 && tiles96 <= 256 && tiles96 > tiles) {
+    c.bn = 96;
     return c;
   }
   // eight compute waves (two per SIMD, so one's promotion FMAs overlap the
@@ -1330,6 +1352,7 @@ int run_decode(Args a, hipStream_t stream) {
   DEC(64, 4)
   DEC(64, 6)
   DEC(128, 4)
+  DEC(96, 4)
   DEC(32, 4)
 #undef DEC
   if (st != FP8GEMM_OK || a.splits == 1) return st;

@@ -95,6 +95,17 @@ def test_dense_exact_small_integers(M, N, K):
     assert (got == want).all(), f"{(got != want).sum()} elements differ"
 
 
+@pytest.mark.parametrize("cfg", ["96,4,1", "32,4,2", "128,4,1,8"])
+@pytest.mark.parametrize("M,N,K", [(64, 300, 512), (128, 2112, 640)])
+def test_dense_decode_variants(M, N, K, cfg, monkeypatch):
+    """BF16 decode instances beyond the defaults (tuning override)."""
+    monkeypatch.setenv("FP8GEMM_DECODE", cfg)
+    seed = 11600 + M + N
+    announce(f"bf16 decode {cfg} {M}x{N}x{K}")
+    A, B = rand_bf16(seed, (M, K)), rand_bf16(seed + 1, (N, K), 0.5)
+    assert_close(gpu_dense(A, B), oracle.gemm_bf16("dense", A, B), f"bf16 decode {cfg}")
+
+
 def test_dense_k_zero_and_empty():
     announce("bf16 dense K=0")
     D = gpu_dense(np.zeros((130, 0), np.uint16), np.zeros((70, 0), np.uint16))

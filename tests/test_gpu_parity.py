@@ -174,8 +174,8 @@ DECODE_VARIANTS = [("FP8GEMM_DECODE", v) for v in
                    ("64,4,1", "64,6,2", "64,6,7", "128,4,3", "64,4,15", "128,4,1", "64,4,4",
                     # eight compute waves (two per SIMD)
                     "128,4,1,8", "128,4,3,8", "64,4,1,8", "64,4,5,8",
-                    # 32 weight rows per tile
-                    "32,4,1", "32,4,3")]
+                    # 32 weight rows per tile; 96 (tiles straddling weight-scale blocks)
+                    "32,4,1", "32,4,3", "96,4,1", "96,4,3")]
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 640), (64, 2112, 1920), (100, 300, 1920),
