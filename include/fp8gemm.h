@@ -31,15 +31,17 @@
  *    Calls are asynchronous on it: a return of FP8GEMM_OK means the work was
  *    enqueued.  No call synchronises or reads device memory on the host, so
  *    every call may be captured into a HIP graph.
- *  - Library-owned memory: the dense call with M <= 128 may split K over
- *    several workgroups; it then enqueues two kernels (partial products,
- *    then their sum in a fixed order, so results are deterministic) and
- *    needs a workspace of 64 MB for the fp32 partials.  It is allocated with hipMalloc
- *    the first time a call on a given (device, stream) needs it, kept until
- *    the process ends, and never allocated while the stream is capturing: a
- *    call made during capture before the stream has a workspace runs
- *    without a K split (same results within the tolerance, slower).  If the
- *    allocation fails the call also runs without a K split.
+ *  - Library-owned memory: the dense calls (FP8 and BF16) may split K over
+ *    several workgroups: with M <= 128 for every tile, and with larger M for
+ *    the tiles of a last, partly filled wave.  They then enqueue two kernels
+ *    (partial products, then their sum in a fixed order, so results are
+ *    deterministic) and need a workspace of 64 MB for the fp32 partials.  It
+ *    is allocated with hipMalloc the first time a call on a given (device,
+ *    stream) needs it, kept until the process ends, and never allocated
+ *    while the stream is capturing: a call made during capture before the
+ *    stream has a workspace runs without a K split (same results within the
+ *    tolerance, slower).  If the allocation fails the call also runs without
+ *    a K split.
  *  - Results are rounded once, fp32 -> bf16, to nearest even; NaN inputs give
  *    NaN outputs.
  *  - Argument errors are reported synchronously, before anything is launched,
