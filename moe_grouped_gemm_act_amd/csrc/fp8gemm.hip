@@ -1132,8 +1132,12 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
 
 // Split-K reduction (decode): D[m][n] = bf16(sum over s, in split order, of
 // ws[s][m][n]).  One thread per 4 consecutive columns of a row; the planes
-// are fetched 8 at a time with buffer loads (planes past S read out of range:
-// zeros, no traffic) so the loads of one thread are issued together.
+// are fetched NB at a time with buffer loads (NB = S up to 8, so no load is
+// wasted; planes past S in a last batch read out of range: zeros, no
+// traffic), so the loads of one thread are issued together.  (Eight loads a
+// batch for every S cost 0.2-0.3 us more per call at S = 4 and 6:
+// out-of-range loads still take the CU's memory request slots.)
+template <int NB>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, uint16_t *D, int M,
                                                             int N, int S) {
   const int nq = (N + 3) / 4;
@@ -1145,10 +1149,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, uin
   const bool vec = (N & 3) == 0;
   const uint32_t off = ((uint32_t)m * N + n) * 4;
   v4f sum = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    v4f p[8];
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    v4f p[NB];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NB; ++k) {
       const uint32_t o = s0 + k < S ? off + (uint32_t)(s0 + k) * plane : OOB;
       if (vec) {
         p[k] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
@@ -1161,7 +1165,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, uin
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NB; ++k) {
       if (s0 + k >= S) break;
 #pragma unroll
       for (int e = 0; e < 4; ++e) sum[e] = s0 + k == 0 ? p[k][e] : sum[e] + p[k][e];
@@ -1357,8 +1361,17 @@ int run_decode(Args a, hipStream_t stream) {
 #undef DEC
   if (st != FP8GEMM_OK || a.splits == 1) return st;
   const long long quads = (long long)a.M * cdiv(a.N, 4);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
-                     stream, a.ws, a.D, a.M, a.N, a.splits);
+  const dim3 grid((unsigned)((quads + 255) / 256));
+  switch (std::min(a.splits, 8)) {
+#define RED(NB_)                                                                                  \
+  case NB_:                                                                                       \
+    hipLaunchKernelGGL(splitk_reduce_kernel<NB_>, grid, dim3(256), 0, stream, a.ws, a.D, a.M, a.N, \
+                       a.splits);                                                                 \
+    break;
+    RED(2) RED(3) RED(4) RED(5) RED(6) RED(7) RED(8)
+#undef RED
+    default: return FP8GEMM_LAUNCH_FAILED;  // unreachable: splits > 1 here
+  }
   return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
