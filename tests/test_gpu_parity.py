@@ -479,11 +479,16 @@ def test_masked_persistent_walk_full(G, M, N, K, walk, monkeypatch):
     assert_close(out[written], ref[written], f"walk {walk} masked G={G}")
 
 
+@pytest.mark.parametrize("walk", ["default", "2"])
 @pytest.mark.parametrize("case", range(len(W.MASKED_CASES)))
-def test_masked_workload_sampled(case):
+def test_masked_workload_sampled(case, walk, monkeypatch):
+    """The masked workload shapes, one workgroup per (tile, expert) and, with
+    FP8GEMM_WALK=2, the persistent walk over the live tiles."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
     G, M, N, K = W.MASKED_CASES[case]
     seed = 5000 + case
-    announce(f"masked G={G} {M}x{N}x{K} seed {seed}")
+    announce(f"masked walk={walk} G={G} {M}x{N}x{K} seed {seed}")
     d = W.masked(seed, G, M, N, K)
     out = gpu_masked(d)
     mm = d["masked_m"]
