@@ -3,7 +3,7 @@
 //
 // Method (DeepGEMM pages, GeekNews summary "Topic Body"): FP8 GEMM with the
 // fine-grained scaling of DeepSeek-V3; the tensor-core partial sum of each
-// scale block is "promoted" into a higher-precision accumulator on the
+// scale block is added (promoted) into a higher-precision accumulator on the
 // general-purpose cores because FP8 tensor-core accumulation is imprecise.
 // The pages describe that schedule for Hopper (TMA staging, warp
 // specialisation, JIT per shape); none of that is reused.  Here:
@@ -24,15 +24,24 @@
 //     an XOR swizzle of the 16-byte chunks so that fragment reads are
 //     bank-conflict free;
 //   * decode shapes (M <= 128) stream the weights from HBM: the same kernel
-//     with 64-row tiles and, where the output gives too few tiles to keep
-//     every CU streaming, a deterministic split of K;
+//     with 32- to 128-row weight tiles sized to fill the CUs and, where the
+//     output alone gives too few tiles, a deterministic split of K summed by
+//     a second kernel;
+//   * large M: 256 x 128 tiles with eight compute waves (two per SIMD, so
+//     one wave's promotion FMAs run beside the other's MFMAs); a partly
+//     filled last wave of tiles is split over K; calls with many tiles and
+//     short K run as a persistent walk, one workgroup per CU, whose loaders
+//     prefetch across tiles;
 //   * the K order inside a block is irrelevant to the sum, so each lane's
 //     32-byte MFMA operand is two 16-byte chunks (c, c+4) of the 128-byte
 //     row and A and B use the same chunk mapping.
 //
 // The grouped layouts reuse the same body (GeekNews "성능 평가"): contiguous
 // tiles look up their expert from m_indices; masked tiles read the expert's
-// device-side row count and tiles past it exit before loading anything.
+// device-side row count and tiles past it exit before loading anything (or
+// the walk visits the live tiles only).  The fused SwiGLU + 1x128
+// requantisation epilogue and a BF16 variant without scales run on the same
+// kernels.
 
 #include <hip/hip_runtime.h>
 #include <atomic>
