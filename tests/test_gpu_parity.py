@@ -480,6 +480,26 @@ def test_masked_persistent_walk_full(G, M, N, K, walk, monkeypatch):
 
 
 @pytest.mark.parametrize("walk", ["default", "2"])
+def test_masked_many_experts_full(walk, monkeypatch):
+    """600 experts: more than the live-tile walk takes, so FP8GEMM_WALK=2
+    falls back to one workgroup per (tile, expert) as the default does."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    G, M, N, K = 600, 40, 130, 256
+    seed = 5400
+    d = W.masked(seed, G, M, N, K)
+    counts = np.random.default_rng(seed).integers(-3, M + 5, G).astype(np.int32)
+    d["masked_m"] = counts
+    announce(f"masked many experts walk={walk} G={G}")
+    out = gpu_masked(d, expected_m=128)
+    ref = oracle.grouped_masked(d["A"], d["sa"], d["B"], d["sb"], counts,
+                                np.full((G, M, N), SENTINEL, np.uint16))
+    written = np.arange(M)[None, :] < np.clip(counts, 0, M)[:, None]
+    assert (out[~written] == SENTINEL).all() and (out[written] != SENTINEL).all()
+    assert_close(out[written], ref[written], f"masked G={G} walk={walk}")
+
+
+@pytest.mark.parametrize("walk", ["default", "2"])
 @pytest.mark.parametrize("case", range(len(W.MASKED_CASES)))
 def test_masked_workload_sampled(case, walk, monkeypatch):
     """The masked workload shapes, one workgroup per (tile, expert) and, with

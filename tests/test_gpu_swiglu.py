@@ -227,6 +227,22 @@ def test_masked_small_full(G, M, I, K, mm):
         compare_masked(A, sa, B, sb, mm, Yk, syk, f"masked G={G} M={M} expected_m={expected_m}")
 
 
+@pytest.mark.parametrize("G", [70, 600])
+def test_masked_many_experts(G):
+    """More experts than one wave scans at once (70: the walk over live
+    tiles) and than the walk takes (600: one workgroup per tile and expert);
+    counts of every kind, tiny experts."""
+    M, I, K = 40, 128, 256
+    seed = 9300 + G
+    rng = np.random.default_rng(seed)
+    mm = rng.integers(-3, M + 5, G).astype(np.int32)
+    mm[:3] = [0, M, 1]
+    announce(f"swiglu masked many experts G={G}")
+    A, sa, B, sb, mm = masked_case(seed, G, M, I, K, mm)
+    Yk, syk = gpu_masked(A, sa, B, sb, mm, 32)
+    compare_masked(A, sa, B, sb, mm, Yk, syk, f"masked G={G}", rows_per_group=4, seed=seed)
+
+
 def test_contiguous_full_size_sampled_rows():
     """the gate/up projection of the contiguous workload (4 experts, 32768
     rows, I = 2048, K = 7168): routing checked on every row, values on
