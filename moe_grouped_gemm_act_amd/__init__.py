@@ -10,6 +10,17 @@ Layouts (row-major, contiguous): A [M,K] and B [N,K] hold e4m3fn codes
 (torch.uint8 or torch.float8_e4m3fn); sa [K/128, M] and sb [ceil(N/128), K/128]
 are float32; D is bfloat16 [M,N].  Grouped forms add a leading G axis as in
 include/fp8gemm.h.
+
+Example (one MoE layer's expert GEMMs on device tensors)::
+
+    import moe_grouped_gemm_act_amd as fg
+    A, sa = fg.quantize_fp8_1x128(x)                # x: bf16 [rows, K]
+    Y, sy = fg.grouped_contiguous_swiglu_fp8(A, sa, W13, s13, m_indices)
+    D = fg.grouped_contiguous(Y, sy, W2, s2, m_indices)  # bf16 [rows, N]
+
+W13 holds each expert's [W_gate; W_up] rows (2I of them), W2 the down
+projection; s13 and s2 are their 128x128 block scales.  Every call enqueues
+on the current stream and may be captured into a HIP graph.
 """
 from __future__ import annotations
 

@@ -297,3 +297,34 @@ def test_masked_full_size_sampled_rows():
     Yk, syk = gpu_masked(d["A"], d["sa"], d["B"], d["sb"], d["masked_m"], d["expected_m"])
     compare_masked(d["A"], d["sa"], d["B"], d["sb"], d["masked_m"], Yk, syk, "masked full size",
                    rows_per_group=2, seed=7)
+
+
+def test_moe_layer_chain():
+    """The calls compose as an MoE expert layer: quantise the activations,
+    gate/up projection with the fused SwiGLU and requantisation, down
+    projection.  The quantiser matches the oracle bit for bit; the down
+    projection, fed the GPU's codes and scales in the layout the SwiGLU call
+    writes them, matches the oracle's GEMM on those operands; padding rows are
+    never written."""
+    from parity_util import SENTINEL, assert_close, bits
+    G, rows, K, I, N = 3, 128 * 4, 512, 256, 384
+    seed = 9400
+    idx, _ = contiguous_indices(seed, G, rows, False)
+    x = np.random.default_rng(seed).standard_normal((rows, K)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    W13, s13 = grouped_weight(seed + 1, G, 2 * I, K)
+    W2, s2 = grouped_weight(seed + 2, G, N, I)
+    announce("MoE layer chain: quantise -> gate/up + SwiGLU -> down")
+    A, sa = fg.quantize_fp8_1x128(xb.cuda())
+    Y, sy = fg.grouped_contiguous_swiglu_fp8(A, sa, to_gpu(W13), to_gpu(s13), to_gpu(idx))
+    D = torch.full((rows, N), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    fg.grouped_contiguous(Y, sy, to_gpu(W2), to_gpu(s2), to_gpu(idx), D)
+    torch.cuda.synchronize()
+    codes, osa = oracle.quantize_1x128(xb.view(torch.int16).numpy().view(np.uint16))
+    assert (A.cpu().numpy() == codes).all() and (sa.cpu().numpy() == osa).all()
+    Yh, syh = Y.cpu().numpy(), sy.cpu().numpy()
+    live = (idx >= 0) & (idx < G)
+    ref = oracle.grouped_contiguous(Yh, syh, W2, s2, idx, np.full((rows, N), SENTINEL, np.uint16))
+    got = bits(D)
+    assert (got[~live] == SENTINEL).all(), "a padding row was written"
+    assert_close(got[live], ref[live], "down projection of the SwiGLU output")
