@@ -1323,9 +1323,10 @@ DecodeCfg decode_config(int M, int N, int Kb, bool bf) {
     return c;
   }
   // eight compute waves (two per SIMD, so one's promotion FMAs overlap the
-  // other's MFMAs) where the tile has the rows for them and K is not split:
-  // 2-4% on 24576x1536 and on 128x7168x2048, slower with a K split
-  // (FP8 only: BF16 has no promotion)
+  // other's MFMAs) where the tile has the rows for them and K is not split
+  // (measured 2-4% with 128-row tiles at 24576x1536 and 64-row tiles at
+  // 128x7168x2048, which now take the narrower tiles above; slower with a K
+  // split); FP8 only: BF16 has no promotion
   if (!bf && c.splits == 1 && decode_built(c.bn, 4, bm, 8)) c.waves = 8;
   return c;
 }
