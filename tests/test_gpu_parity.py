@@ -531,6 +531,25 @@ def test_masked_workload_sampled(case, walk, monkeypatch):
 # ------------------------------------------------- K past the tile kernel ----
 
 
+def test_longest_k_of_the_tile_kernel():
+    """K = 20480 (160 blocks), the longest K whose weight scales the tile
+    kernel preloads: a decode shape (K split), a large-M shape with a tail
+    split, and a contiguous call."""
+    K = 20480
+    for (M, N, seed) in ((64, 256, 1950), (200, 520, 1951)):
+        announce(f"longest tile-kernel K dense {M}x{N}x{K}")
+        d = W.dense(seed, M, N, K)
+        assert_close(gpu_dense(d), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), f"K={K} {M}x{N}")
+    announce(f"longest tile-kernel K contiguous G=2 256x260x{K}")
+    c = W.contiguous(1952, 2, 256, 260, K, uniform=False)
+    out = gpu_contig(c)
+    ref = oracle.grouped_contiguous(c["A"], c["sa"], c["B"], c["sb"], c["m_indices"],
+                                    np.full((c["M"], c["N"]), SENTINEL, np.uint16))
+    pad = c["m_indices"] < 0
+    assert (out[pad] == SENTINEL).all() and (out[~pad] != SENTINEL).all()
+    assert_close(out[~pad], ref[~pad], f"K={K} contiguous")
+
+
 def test_long_k_fallback_all_layouts():
     """K = 20608 (161 blocks) is past the tile kernel's weight-scale preload:
     the register-staged fallback kernel serves all three layouts."""
