@@ -1247,10 +1247,16 @@ const Workspace *workspace(hipStream_t s) {
   auto it = g_ws.find({dev, s});
   if (it != g_ws.end()) return &it->second;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  Workspace w;
-  if (hipMalloc(reinterpret_cast<void **>(&w.part), WS_FLOATS * sizeof(float)) != hipSuccess)
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // handled as capturing: no workspace, no K split
     return nullptr;
+  }
+  if (cs != hipStreamCaptureStatusNone) return nullptr;
+  Workspace w;
+  if (hipMalloc(reinterpret_cast<void **>(&w.part), WS_FLOATS * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();  // handled: the call runs without a K split
+    return nullptr;
+  }
   return &(g_ws[{dev, s}] = w);
 }
 
@@ -1372,17 +1378,19 @@ int run_decode(Args a, hipStream_t stream) {
   if (st != FP8GEMM_OK || a.splits == 1) return st;
   const long long quads = (long long)a.M * cdiv(a.N, 4);
   const dim3 grid((unsigned)((quads + 255) / 256));
+  // the launch's own status (hipGetLastError would also report an earlier
+  // call's error)
+  void *rargs[] = {&a.ws, &a.D, &a.M, &a.N, &a.splits};
+  const void *red = nullptr;
   switch (std::min(a.splits, 8)) {
-#define RED(NB_)                                                                                  \
-  case NB_:                                                                                       \
-    hipLaunchKernelGGL(splitk_reduce_kernel<NB_>, grid, dim3(256), 0, stream, a.ws, a.D, a.M, a.N, \
-                       a.splits);                                                                 \
-    break;
+#define RED(NB_)                                                                   \
+  case NB_: red = reinterpret_cast<const void *>(&splitk_reduce_kernel<NB_>); break;
     RED(2) RED(3) RED(4) RED(5) RED(6) RED(7) RED(8)
 #undef RED
     default: return FP8GEMM_LAUNCH_FAILED;  // unreachable: splits > 1 here
   }
-  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+  return hipLaunchKernel(red, grid, dim3(256), rargs, 0, stream) == hipSuccess ? FP8GEMM_OK
+                                                                             : FP8GEMM_LAUNCH_FAILED;
 }
 
 template <int BM, int BN, int LAYOUT>
@@ -1480,9 +1488,11 @@ int launch_dense_large(Args a, hipStream_t stream) {
         dim3(a.full_tiles + R * a.tail_splits), dim3((WGN * WGM + NLD) * 64), kargs, 0, stream);
   }
   if (er != hipSuccess) return FP8GEMM_LAUNCH_FAILED;
-  hipLaunchKernelGGL((tail_reduce_kernel<BM, BN>), dim3(R * (BM * BN / 4) / 256), dim3(256), 0, stream,
-                     a.ws, a.D, a.M, a.N, a.full_tiles, a.tail_splits, tiles_m, tiles_n);
-  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+  int tm = tiles_m, tn = tiles_n;
+  void *rargs[] = {&a.ws, &a.D, &a.M, &a.N, &a.full_tiles, &a.tail_splits, &tm, &tn};
+  er = hipLaunchKernel(reinterpret_cast<const void *>(&tail_reduce_kernel<BM, BN>),
+                       dim3(R * (BM * BN / 4) / 256), dim3(256), rargs, 0, stream);
+  return er == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
 
 // Contiguous layout, 256 x 128 tiles: the persistent walk when there are

@@ -93,8 +93,11 @@ extern "C" int quantize_fp8_1x128(const void *X, void *A, float *sa, int M, int 
       reinterpret_cast<uintptr_t>(sa) % 4)
     return FP8GEMM_MISALIGNED;
   if ((M + QROWS - 1) / QROWS > 65535) return FP8GEMM_UNSUPPORTED_SHAPE;
-  hipLaunchKernelGGL(quant_kernel, dim3(K / 128, (M + QROWS - 1) / QROWS), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(X),
-                     static_cast<uint8_t *>(A), sa, M, K);
-  return hipGetLastError() == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
+  const uint16_t *x = static_cast<const uint16_t *>(X);
+  uint8_t *a = static_cast<uint8_t *>(A);
+  void *args[] = {&x, &a, &sa, &M, &K};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&quant_kernel),
+                                       dim3(K / 128, (M + QROWS - 1) / QROWS), dim3(256), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8GEMM_OK : FP8GEMM_LAUNCH_FAILED;
 }
