@@ -69,7 +69,8 @@ enum fp8gemm_status {
   FP8GEMM_INVALID_ARG = 1,       /* null pointer for a non-empty problem, negative size, G < 1, expected_m < 0 */
   FP8GEMM_UNSUPPORTED_SHAPE = 2, /* K % 128 != 0; contiguous layout with M % 128 != 0; sizes past 2^31 elements */
   FP8GEMM_MISALIGNED = 3,        /* A, B or D not 16-byte aligned, sa or sb not 4-byte aligned */
-  FP8GEMM_LAUNCH_FAILED = 4      /* the HIP runtime refused the launch */
+  FP8GEMM_LAUNCH_FAILED = 4      /* the HIP runtime refused one of the call's own launches (an
+                                    error left by an earlier HIP call is not reported) */
 };
 
 /*
