@@ -35,13 +35,24 @@
  *    several workgroups: with M <= 128 for every tile, and with larger M for
  *    the tiles of a last, partly filled wave.  They then enqueue two kernels
  *    (partial products, then their sum in a fixed order, so results are
- *    deterministic) and need a workspace of 64 MB for the fp32 partials.  It
- *    is allocated with hipMalloc the first time a call on a given (device,
- *    stream) needs it, kept until the process ends, and never allocated
- *    while the stream is capturing: a call made during capture before the
- *    stream has a workspace runs without a K split (same results within the
- *    tolerance, slower).  If the allocation fails the call also runs without
- *    a K split.
+ *    deterministic) and keep the fp32 partials in a 32 MB library workspace:
+ *      . calls made outside graph capture share one workspace per device,
+ *        allocated with hipMalloc on first need and kept until the process
+ *        ends.  Its users are ordered on the GPU: a call on a stream other
+ *        than the previous user's makes its stream wait (hipStreamWaitEvent)
+ *        for an event recorded after that user's kernels, so split calls on
+ *        different streams never share partials at once (they run one after
+ *        the other) and memory does not grow with the number of streams;
+ *      . calls captured into a HIP graph use a workspace of that capture
+ *        (one per capture and capturing stream), taken from workspaces that
+ *        destroyed graphs gave back, else allocated during the capture with
+ *        hipMalloc (the thread's capture mode is switched to relaxed for that
+ *        one call and restored).  The graph holds it through a user object:
+ *        it returns to the library when the graph and every executable
+ *        instantiated from it have been destroyed.  A replay, on any stream,
+ *        therefore never shares partials with eager calls or other graphs.
+ *    If no workspace can be had, the call runs without a K split (the same
+ *    results within the tolerance, slower).
  *  - Results are rounded once, fp32 -> bf16, to nearest even; NaN inputs give
  *    NaN outputs.
  *  - Argument errors are reported synchronously, before anything is launched,
@@ -52,8 +63,9 @@
  *  - Constraints: M, N, K >= 0; K % 128 == 0; A, B and D 16-byte aligned;
  *    sa and sb 4-byte aligned.  M == 0 or N == 0 returns FP8GEMM_OK without
  *    launching; K == 0 writes zeros (an empty sum).
- *  - Calls on different streams may overlap: each (device, stream) has its
- *    own workspace.  Calls on one stream are ordered by the stream.
+ *  - Calls on different streams may overlap, except that split calls made
+ *    outside capture are ordered through the device workspace as above.
+ *    Calls on one stream are ordered by the stream.
  */
 #ifndef FP8GEMM_H
 #define FP8GEMM_H

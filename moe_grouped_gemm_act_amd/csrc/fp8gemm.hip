@@ -52,6 +52,7 @@
 #include <cstdlib>
 #include <map>
 #include <mutex>
+#include <vector>
 
 #include "e4m3.h"
 #include "fp8gemm.h"
@@ -1228,37 +1229,194 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float *ws, uint1
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// ---- split-K workspace: one per (device, stream), made on first need ------
-// Holds the fp32 partial planes of a split call.  Never allocated while the
-// stream is capturing: such calls run without a K split instead.
-constexpr size_t WS_FLOATS = size_t(16) << 20;  // 64 MB of partials
+// ---- split-K workspace -------------------------------------------------
+// The fp32 partials of a split call (decode planes, or the tail parts of a
+// large-M call) live in a library-owned workspace of WS_BYTES, which every
+// default plan fits (decode: splits x M x N <= 256 x 128 x 128 floats = 16 MB;
+// tail: at most 256 parts of 256 x 128 floats = 32 MB).
+//   * Eager calls (stream not capturing) share ONE workspace per device,
+//     allocated on first need.  Its users are ordered on the GPU: a call on a
+//     stream other than the last user's first makes its stream wait for the
+//     event the last user recorded after its kernels, then records the event
+//     itself.  So split calls on different streams run one after the other
+//     (never on the same partials at once), and memory does not grow with the
+//     number of streams.
+//   * Calls made while their stream is being captured into a graph take a
+//     workspace of their own for that capture (one per capture and capturing
+//     stream, shared by the capture's split calls on that stream, which the
+//     stream orders).  It comes from the device's list of workspaces released
+//     by graphs that have been destroyed, else from hipMalloc with this
+//     thread's capture mode exchanged to relaxed for the allocation (an
+//     allocation is not a stream operation; global mode forbids it only as
+//     potentially unsafe).  The graph holds it through a user object whose
+//     release (when the graph and every executable made from it are
+//     destroyed) puts it back on the list; the release callback makes no HIP
+//     call.  A replay therefore never shares partials with eager calls or with
+//     another graph.
+//   * When no workspace can be had, the call runs without a K split (the
+//     same results within the tolerance, slower).
+// (Graph memory nodes from a captured hipMallocAsync would be the plain
+// route; on this runtime a second launch of such a graph faulted, so they
+// are not used.)
+constexpr size_t WS_BYTES = size_t(32) << 20;
+constexpr size_t WS_FLOATS = WS_BYTES / sizeof(float);
+constexpr int MAX_DEV = 64;
 
-struct Workspace {
-  float *part = nullptr;
+struct DeviceWs {
+  std::mutex mu;  // eager workspace and event; held across an eager split call's launches
+  float *eager = nullptr;
+  hipEvent_t done = nullptr;     // recorded after the last eager user's kernels
+  hipStream_t last = nullptr;    // the stream that recorded it
+  bool recorded = false;
+  // capture workspaces; guarded by cap_mu, never held across a HIP call, so
+  // the user-object release callback may take it
+  std::mutex cap_mu;
+  std::map<std::pair<unsigned long long, hipStream_t>, float *> live;  // (capture id, stream)
+  std::vector<float *> spare;    // released by destroyed graphs, reusable
+};
+DeviceWs g_dev_ws[MAX_DEV];
+
+struct CaptureWsRecord {  // owned by the user object
+  int dev;
+  unsigned long long id;
+  hipStream_t stream;
+  float *ptr;
 };
 
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-
-const Workspace *workspace(hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  auto it = g_ws.find({dev, s});
-  if (it != g_ws.end()) return &it->second;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
-    (void)hipGetLastError();  // handled as capturing: no workspace, no K split
-    return nullptr;
+void release_capture_ws(void *p) {  // user-object destructor: no HIP calls
+  CaptureWsRecord *r = static_cast<CaptureWsRecord *>(p);
+  DeviceWs &d = g_dev_ws[r->dev];
+  {
+    std::lock_guard<std::mutex> lk(d.cap_mu);
+    d.live.erase({r->id, r->stream});
+    d.spare.push_back(r->ptr);
   }
-  if (cs != hipStreamCaptureStatusNone) return nullptr;
-  Workspace w;
-  if (hipMalloc(reinterpret_cast<void **>(&w.part), WS_FLOATS * sizeof(float)) != hipSuccess) {
-    (void)hipGetLastError();  // handled: the call runs without a K split
-    return nullptr;
-  }
-  return &(g_ws[{dev, s}] = w);
+  delete r;
 }
+
+// A workspace held for one call.  acquire() returns false when the call must
+// run unsplit; release() (after the call's launches) completes the eager
+// ordering.
+struct WsLease {
+  float *ptr = nullptr;
+  DeviceWs *eager_dev = nullptr;  // set for eager leases: d.mu is held until release
+  hipStream_t stream = nullptr;
+
+  bool acquire(hipStream_t s) {
+    stream = s;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
+      (void)hipGetLastError();
+      return false;
+    }
+    DeviceWs &d = g_dev_ws[dev];
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    unsigned long long id = 0;
+    hipGraph_t graph = nullptr;
+    const hipGraphNode_t *deps = nullptr;
+    size_t ndeps = 0;
+    if (hipStreamGetCaptureInfo_v2(s, &cs, &id, &graph, &deps, &ndeps) != hipSuccess) {
+      (void)hipGetLastError();  // handled: no split
+      return false;
+    }
+    if (cs == hipStreamCaptureStatusActive) return acquire_capture(d, dev, id, graph);
+    if (cs != hipStreamCaptureStatusNone) return false;  // an invalidated capture
+    d.mu.lock();
+    if (!d.eager) {
+      if (hipMalloc(reinterpret_cast<void **>(&d.eager), WS_BYTES) != hipSuccess) {
+        (void)hipGetLastError();  // handled: no split
+        d.eager = nullptr;
+        d.mu.unlock();
+        return false;
+      }
+    }
+    if (!d.done && hipEventCreateWithFlags(&d.done, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      d.done = nullptr;
+      d.mu.unlock();
+      return false;
+    }
+    if (d.recorded && d.last != s && hipStreamWaitEvent(s, d.done, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      d.mu.unlock();
+      return false;
+    }
+    ptr = d.eager;
+    eager_dev = &d;
+    return true;
+  }
+
+  bool acquire_capture(DeviceWs &d, int dev, unsigned long long id, hipGraph_t graph) {
+    {
+      std::lock_guard<std::mutex> lk(d.cap_mu);
+      auto it = d.live.find({id, stream});
+      if (it != d.live.end()) {
+        ptr = it->second;
+        return true;
+      }
+      if (!d.spare.empty()) {
+        ptr = d.spare.back();
+        d.spare.pop_back();
+      }
+    }
+    if (!ptr) {
+      hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+      if (hipThreadExchangeStreamCaptureMode(&mode) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+      }
+      const hipError_t e = hipMalloc(reinterpret_cast<void **>(&ptr), WS_BYTES);
+      hipStreamCaptureMode back = mode;
+      (void)hipThreadExchangeStreamCaptureMode(&back);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        ptr = nullptr;
+        return false;
+      }
+    }
+    CaptureWsRecord *r = new CaptureWsRecord{dev, id, stream, ptr};
+    hipUserObject_t uo = nullptr;
+    if (hipUserObjectCreate(&uo, r, release_capture_ws, 1, hipUserObjectNoDestructorSync) != hipSuccess) {
+      (void)hipGetLastError();
+      std::lock_guard<std::mutex> lk(d.cap_mu);
+      d.spare.push_back(ptr);
+      delete r;
+      ptr = nullptr;
+      return false;
+    }
+    {
+      std::lock_guard<std::mutex> lk(d.cap_mu);
+      d.live[{id, stream}] = ptr;
+    }
+    if (hipGraphRetainUserObject(graph, uo, 1, hipGraphUserObjectMove) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipUserObjectRelease(uo, 1);  // runs release_capture_ws: back on the list
+      ptr = nullptr;
+      return false;
+    }
+    return true;
+  }
+
+  // after the call's launches (whatever their status)
+  void release() {
+    if (!eager_dev) return;
+    DeviceWs &d = *eager_dev;
+    if (hipEventRecord(d.done, stream) == hipSuccess) {
+      d.recorded = true;
+      d.last = stream;
+    } else {
+      // the next user on another stream cannot be ordered after this call:
+      // wait for it here (eager only, and only on a runtime error)
+      (void)hipGetLastError();
+      (void)hipStreamSynchronize(stream);
+      (void)hipGetLastError();
+      d.recorded = false;
+    }
+    eager_dev = nullptr;
+    d.mu.unlock();
+  }
+  ~WsLease() { release(); }
+};
 
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool KSPLIT = false,
           bool ACT = false, bool BF = false>
@@ -1348,13 +1506,13 @@ int run_decode(Args a, hipStream_t stream) {
   splits = Kb > 0 ? cdiv(Kb, kps) : 1;
   a.splits = splits;
   a.kb_per_split = kps;
+  WsLease ws;  // held until the reduction is enqueued
   if (splits > 1) {
-    const Workspace *w = workspace(stream);
-    if (!w || (size_t)splits * a.M * a.N > WS_FLOATS) {
+    if ((size_t)splits * a.M * a.N > WS_FLOATS || !ws.acquire(stream)) {
       a.splits = 1;
       a.kb_per_split = Kb;
     } else {
-      a.ws = w->part;
+      a.ws = ws.ptr;
     }
   }
   int st = FP8GEMM_LAUNCH_FAILED;  // unreachable: decode_config returns built instances only
@@ -1449,7 +1607,7 @@ hipError_t launch_walk(Args &a, int P, hipStream_t stream) {
 // wave of R <= 128 tiles for the 256 CUs, those R tiles are split over K into
 // S = min(8, 256 / R) parts (each at least 4 K blocks) that run as the last
 // items of the same grid, and tail_reduce_kernel adds the parts.  Without a
-// workspace (first call on a stream under capture) the tail is not split.
+// workspace the tail is not split.
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool BF = false>
 int launch_dense_large(Args a, hipStream_t stream) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
@@ -1457,8 +1615,8 @@ int launch_dense_large(Args a, hipStream_t stream) {
   const int Kb = (BF ? 2 * a.K : a.K) / BK, R = T % 256;
   int S = R > 0 && R <= 128 ? std::min(8, 256 / R) : 1;
   while (S > 1 && cdiv(Kb, S) < 4) --S;
-  const Workspace *w = S > 1 ? workspace(stream) : nullptr;
-  if (S > 1 && (!w || (size_t)R * S * BM * BN > WS_FLOATS)) S = 1;
+  WsLease ws;  // held until the tail reduction is enqueued
+  if (S > 1 && ((size_t)R * S * BM * BN > WS_FLOATS || !ws.acquire(stream))) S = 1;
   // more tiles than CUs: the persistent walk over the same items
   const int P = walk_workgroups();
   const bool walk = walk_enabled(BF ? 2 * a.K : a.K) && P >= 8 && T > P;
@@ -1476,7 +1634,7 @@ int launch_dense_large(Args a, hipStream_t stream) {
   a.full_tiles = T - R;
   a.tail_splits = cdiv(Kb, kb);
   a.tail_kb = kb;
-  a.ws = w->part;
+  a.ws = ws.ptr;
   hipError_t er;
   if (walk) {
     er = launch_walk<WGN, WGM, TN, TM, STAGES, NLD, DENSE, BF>(a, P, stream);

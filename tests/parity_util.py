@@ -35,6 +35,44 @@ def f32(b):
     return oracle.bf16_bits_to_float(b)
 
 
+def assert_close_full(out_bits, ref_bits, what="", chunk=1 << 23):
+    """assert_close over arrays of any size, in chunks: the same element bound
+    (with rms(ref) over all compared elements) and the relative Frobenius
+    error over all of them.  Returns the Frobenius error."""
+    o_all = np.asarray(out_bits).reshape(-1)
+    r_all = np.asarray(ref_bits).reshape(-1)
+    assert o_all.shape == r_all.shape, f"{what}: shapes differ"
+    n = r_all.size
+    sq, cnt = 0.0, 0
+    for i in range(0, n, chunk):
+        o, r = f32(o_all[i:i + chunk]), f32(r_all[i:i + chunk])
+        nan_o, nan_r = np.isnan(o), np.isnan(r)
+        assert (nan_o == nan_r).all(), \
+            f"{what}: NaN pattern differs at {i + np.flatnonzero(nan_o != nan_r)[:10]}"
+        r = r[~nan_r].astype(np.float64)
+        sq += float(np.dot(r, r))
+        cnt += r.size
+    if cnt == 0:
+        return 0.0
+    rms = (sq / cnt) ** 0.5
+    esq, bad, first = 0.0, 0, None
+    for i in range(0, n, chunk):
+        o, r = f32(o_all[i:i + chunk]).astype(np.float64), f32(r_all[i:i + chunk]).astype(np.float64)
+        keep = ~np.isnan(r)
+        o, r, pos = o[keep], r[keep], np.flatnonzero(keep) + i
+        e = np.abs(o - r)
+        esq += float(np.dot(e, e))
+        over = np.flatnonzero(e > REL_ELEM * np.abs(r) + ABS_RMS * rms)
+        if over.size and first is None:
+            first = (pos[over[:5]], o[over[:5]], r[over[:5]])
+        bad += over.size
+    assert bad == 0, (f"{what}: {bad} of {cnt} elements out of tolerance; first at flat index "
+                      f"{first[0]} out={first[1]} ref={first[2]}")
+    frob = esq ** 0.5 / sq ** 0.5 if sq > 0 else esq ** 0.5
+    assert frob <= FROB, f"{what}: relative Frobenius error {frob:.3e} over {cnt} elements"
+    return frob
+
+
 def assert_close(out_bits, ref_bits, what=""):
     out_bits = np.asarray(out_bits).ravel()
     ref_bits = np.asarray(ref_bits).ravel()

@@ -29,7 +29,7 @@ def replay_equals_eager(what, call, outs):
         o.zero_()  # rows a call does not write (padding, masked) must compare equal too
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        call()  # eager first: any per-stream workspace is made outside capture
+        call()
     s.synchronize()
     eager = [o.clone() for o in outs]
     g = torch.cuda.CUDAGraph()
@@ -96,10 +96,11 @@ def test_graph_bf16_dense(M, N, K):
     replay_equals_eager(f"bf16 {M}x{N}x{K}", lambda: fg.gemm_bf16_nt(a, b, D), [D])
 
 
-def test_capture_before_any_workspace_runs_unsplit():
-    """A split-K shape captured on a stream that has never run an eager call
-    has no workspace yet: the captured launch runs without a K split (no
-    allocation during capture) and still matches the oracle."""
+def test_capture_takes_its_own_workspace():
+    """A split-K shape captured on a fresh stream before any eager call: the
+    capture takes a workspace of its own (allocated during the capture), so
+    every replay, with eager calls of the same shape in between, equals the
+    eager result bit for bit and matches the oracle."""
     import oracle
     from parity_util import assert_close, bits, sentinel_out
     M, N, K = 64, 2112, 7168
@@ -111,20 +112,109 @@ def test_capture_before_any_workspace_runs_unsplit():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
-    with torch.cuda.stream(s):
-        g.replay()
-    s.synchronize()
-    rng = np.random.default_rng(8850)
-    pm, pn = rng.integers(0, M, 3000), rng.integers(0, N, 3000)
-    got = bits(D)
-    assert_close(got[pm, pn], oracle.points("dense", d["A"], d["sa"], d["B"], d["sb"], pm, pn),
-                 "captured without a workspace")
-    announce("capture before any workspace: matches the oracle")
+    De = sentinel_out((M, N))
+    fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, De)
+    torch.cuda.synchronize()
+    eager = bits(De)
+    for r in range(3):
+        D.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        assert (bits(D) == eager).all(), f"replay {r}"
+        fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, De)
+        torch.cuda.synchronize()
+    assert_close(eager, oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), "captured first")
+    announce("capture before any eager call: own workspace, replays equal eager and oracle")
+
+
+def test_graph_replay_beside_eager_calls_on_another_stream():
+    """A graph of split calls (decode planes and a large-M tail split)
+    captured on stream A is replayed on stream B while eager split calls run
+    on stream A, with no synchronisation between them: both results equal
+    the same calls made one at a time."""
+    from parity_util import bits, sentinel_out
+    shapes = [(128, 4096, 7168, 8880), (1100, 7400, 2048, 8881), (64, 2112, 7168, 8882),
+              (300, 520, 2048, 8883)]
+    ins = []
+    for M, N, K, seed in shapes:
+        d = W.dense(seed, M, N, K)
+        ins.append(((to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"])), (M, N)))
+    ref = []
+    for args, mn in ins:
+        D = sentinel_out(mn)
+        fg.gemm_fp8_1x128_128x128_bf16(*args, D)
+        torch.cuda.synchronize()
+        ref.append(bits(D))
+    sa_, sb_ = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [sentinel_out(mn) for _, mn in ins]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=sa_):  # the graph: shapes 0 and 1
+        for (args, _), D in zip(ins[:2], outs[:2]):
+            fg.gemm_fp8_1x128_128x128_bf16(*args, D)
+    for o in outs:
+        o.zero_()
+    torch.cuda.synchronize()
+    announce("graph on stream B beside eager split calls on stream A")
+    for _ in range(6):
+        with torch.cuda.stream(sb_):
+            g.replay()
+        with torch.cuda.stream(sa_):  # eager: shapes 2 and 3
+            for (args, _), D in zip(ins[2:], outs[2:]):
+                fg.gemm_fp8_1x128_128x128_bf16(*args, D)
+    torch.cuda.synchronize()
+    for i, (D, r) in enumerate(zip(outs, ref)):
+        assert (bits(D) == r).all(), f"shape {shapes[i][:3]} differs from its serial result"
+
+
+def test_workspace_memory_flat():
+    """Split calls on 100 streams made and dropped one after another, and 12
+    graphs of a split call captured, replayed and destroyed: the device's free
+    memory does not shrink by more than one workspace (32 MB) over each."""
+    import gc
+    import time
+    from parity_util import sentinel_out
+    M, N, K = 128, 2112, 7168
+    d = W.dense(8890, M, N, K)
+    A, sa, B, sb = (to_gpu(d[k]) for k in ("A", "sa", "B", "sb"))
+    D = sentinel_out((M, N))
+    fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)  # the device's eager workspace exists
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for _ in range(100):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
+        s.synchronize()
+        del s
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert free0 - free1 <= (32 << 20), f"100 streams: free memory fell by {(free0 - free1) >> 20} MB"
+    s = torch.cuda.Stream()
+    for i in range(12):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fg.gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D)
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        del g
+        gc.collect()
+        torch.cuda.synchronize()
+        time.sleep(0.02)  # the graph's release callback may run on a runtime thread
+        if i == 0:
+            free2 = torch.cuda.mem_get_info()[0]
+    free3 = torch.cuda.mem_get_info()[0]
+    assert free2 - free3 <= (32 << 20), f"11 more graphs: free memory fell by {(free2 - free3) >> 20} MB"
+    announce(f"memory: streams {(free0 - free1) >> 20} MB, graphs {(free2 - free3) >> 20} MB")
 
 
 def test_two_streams_split_k_concurrently():
-    """Split-K calls on two streams at once use separate workspaces: both
-    results equal the same calls made one after the other."""
+    """Split-K calls on two streams interleaved with no synchronisation: the
+    device's one eager workspace orders them on the GPU, so both results equal
+    the same calls made one after the other."""
     from parity_util import bits, sentinel_out
     shapes = [(64, 2112, 7168, 8860), (128, 4096, 7168, 8861)]
     ins = []
@@ -152,7 +242,7 @@ def test_two_streams_split_k_concurrently():
 
 def test_graph_persistent_walk_calls():
     """The persistent walk under capture: a dense call with a tail split
-    (workspace made by the eager call before capture), a contiguous call and
+    (its partials in the capture's own workspace), a contiguous call and
     a contiguous SwiGLU call, each with more tiles than CUs."""
     d = W.dense(8870, 1100, 7400, 2048)  # 261 tiles: 256 whole + 5 split in 4
     A, sa, B, sb = (to_gpu(d[k]) for k in ("A", "sa", "B", "sb"))

@@ -69,17 +69,16 @@ def test_quant_special_blocks():
     check(xb, "special blocks")
 
 
-def test_quant_prefill_activation_sampled_rows():
+def test_quant_prefill_activation_full():
     M, K = 4096, 7168
     x = synth.normal(7100, M * K).reshape(M, K)
     x[synth.heavy_rows(7107, M) > 1] *= 50
     xb = bf16_bits(x)
-    announce("quant 4096x7168 sampled rows")
+    announce("quant 4096x7168")
     A, gsa = gpu_quant(xb)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, M - 1], np.random.default_rng(7).integers(0, M, 40)]))
-    codes, sa = oracle.quantize_1x128(np.ascontiguousarray(xb[rows]))
-    assert (A[rows] == codes).all()
-    assert (gsa[:, rows].view(np.uint32) == sa.view(np.uint32)).all()
+    codes, sa = oracle.quantize_1x128(xb)
+    assert (A == codes).all()
+    assert (gsa.view(np.uint32) == sa.view(np.uint32)).all()
 
 
 def test_quant_stream_and_determinism():

@@ -47,7 +47,7 @@ def test_earlier_hip_error_is_not_reported():
         ("quantize 300x1024", lambda: fg.quantize_fp8_1x128(X, QA, Qs), QA),
     ]
     ref = []
-    for what, call, out in calls:  # eager first: workspaces exist before the failed allocation
+    for what, call, out in calls:  # eager first: the workspace exists before the failed allocation
         call()
         torch.cuda.synchronize()
         ref.append(bits(out) if out.dtype == torch.bfloat16 else out.cpu().numpy())

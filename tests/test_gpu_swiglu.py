@@ -126,6 +126,16 @@ def oracle_rows(A, sa, B, sb, idx):
     return Yo, syo, silu_mul(h, I)
 
 
+def check_rows_chunked(Yk, syk, Yo, syo, y64, what, chunk=4096):
+    """check_rows over row chunks (bounded memory for whole workloads)"""
+    R = Yk.shape[0]
+    for r0 in range(0, R, chunk):
+        r1 = min(R, r0 + chunk)
+        check_rows(Yk[r0:r1], np.ascontiguousarray(syk[:, r0:r1]), Yo[r0:r1],
+                   np.ascontiguousarray(syo[:, r0:r1]), y64[r0:r1],
+                   what if R <= chunk else f"{what} rows {r0}..{r1 - 1}")
+
+
 def compare_contig(A, sa, B, sb, idx, Yk, syk, what):
     Yo, syo, y64 = oracle_rows(A, sa, B, sb, idx)
     G = B.shape[0]
@@ -133,7 +143,7 @@ def compare_contig(A, sa, B, sb, idx, Yk, syk, what):
     assert (Yk[~live] == CODE_SENT).all(), f"{what}: a padding row was written"
     assert (syk[:, ~live].view(np.uint32) == SCALE_SENT).all(), f"{what}: a padding scale was written"
     if live.any():
-        check_rows(Yk[live], syk[:, live], Yo[live], syo[:, live], y64[live], what)
+        check_rows_chunked(Yk[live], syk[:, live], Yo[live], syo[:, live], y64[live], what)
 
 
 @pytest.mark.parametrize("G,rows,I,K,uniform", [
@@ -210,7 +220,7 @@ def compare_masked(A, sa, B, sb, mm, Yk, syk, what, rows_per_group=None, seed=0)
     sas = np.ascontiguousarray(sa[pg, :, pm].T)
     idx = pg.astype(np.int32)
     Yo, syo, y64 = oracle_rows(As, sas, B, sb, idx)
-    check_rows(Yk[pg, pm], np.ascontiguousarray(syk[pg, :, pm].T), Yo, syo, y64, what)
+    check_rows_chunked(Yk[pg, pm], np.ascontiguousarray(syk[pg, :, pm].T), Yo, syo, y64, what)
 
 
 @pytest.mark.parametrize("G,M,I,K,mm", [
@@ -243,60 +253,34 @@ def test_masked_many_experts(G):
     compare_masked(A, sa, B, sb, mm, Yk, syk, f"masked G={G}", rows_per_group=4, seed=seed)
 
 
-def test_contiguous_full_size_sampled_rows():
-    """the gate/up projection of the contiguous workload (4 experts, 32768
-    rows, I = 2048, K = 7168): routing checked on every row, values on
-    sampled rows"""
-    G, rows, N, K, uniform = W.CONTIG_CASES[0]
+@pytest.mark.parametrize("case", range(len(W.CONTIG_CASES)))
+def test_contiguous_workload_full(case):
+    """the gate/up projection of the contiguous workloads (4 experts x 8192
+    rows, and 8 uneven padded experts; 32768 rows, I = 2048, K = 7168):
+    every padding row untouched, every routed row's codes and scales checked
+    against the oracle"""
+    G, rows, N, K, uniform = W.CONTIG_CASES[case]
     I = N // 2
-    seed = 3000
+    seed = 3000 + 100 * case
     announce(f"swiglu contiguous full size G={G} rows={rows} I={I} K={K} seed {seed}")
     d = W.contiguous(seed, G, rows, N, K, uniform)
     Yk, syk = gpu_contig(d["A"], d["sa"], d["B"], d["sb"], d["m_indices"])
-    rng = np.random.default_rng(5)
-    pick = np.unique(np.concatenate([[0, 127, 128, rows - 1],
-                                     [s for (st, _, v) in d["segments"] for s in (st, st + v - 1)],
-                                     rng.integers(0, rows, 16)]))
-    idx = d["m_indices"]
-    A = np.ascontiguousarray(d["A"][pick])
-    sa = np.ascontiguousarray(d["sa"][:, pick])
-    Yo, syo, y64 = oracle_rows(A, sa, d["B"], d["sb"], idx[pick])
-    live = (idx >= 0) & (idx < G)
-    assert (Yk[~live] == CODE_SENT).all()
-    lp = (idx[pick] >= 0) & (idx[pick] < G)
-    check_rows(Yk[pick][lp], syk[:, pick][:, lp], Yo[lp], syo[:, lp], y64[lp], "contiguous full size")
-
-
-def test_contiguous_ragged_full_size_routing():
-    """the 8-expert ragged contiguous workload: every padding row untouched,
-    every routed row written, values on sampled rows"""
-    G, rows, N, K, uniform = W.CONTIG_CASES[1]
-    I = N // 2
-    seed = 3100
-    announce(f"swiglu contiguous ragged G={G} rows={rows} I={I} K={K} seed {seed}")
-    d = W.contiguous(seed, G, rows, N, K, uniform)
-    Yk, syk = gpu_contig(d["A"], d["sa"], d["B"], d["sb"], d["m_indices"])
     idx = d["m_indices"]
     live = (idx >= 0) & (idx < G)
-    assert (Yk[~live] == CODE_SENT).all() and (syk[:, ~live].view(np.uint32) == SCALE_SENT).all()
     assert (Yk[live] != CODE_SENT).all() and np.isfinite(syk[:, live]).all()
-    pick = np.flatnonzero(live)[np.random.default_rng(6).choice(live.sum(), 12, replace=False)]
-    Yo, syo, y64 = oracle_rows(np.ascontiguousarray(d["A"][pick]),
-                               np.ascontiguousarray(d["sa"][:, pick]), d["B"], d["sb"], idx[pick])
-    check_rows(Yk[pick], syk[:, pick], Yo, syo, y64, "contiguous ragged full size")
+    compare_contig(d["A"], d["sa"], d["B"], d["sb"], idx, Yk, syk, f"contiguous G={G} full size")
 
 
-def test_masked_full_size_sampled_rows():
+def test_masked_workload_full():
     """the masked workload's gate/up projection (16 experts, 256-row
-    capacity, I = 2048, K = 7168)"""
+    capacity, I = 2048, K = 7168): every valid row of every expert"""
     G, M, N, K = W.MASKED_CASES[0]
     I = N // 2
     seed = 4000
     announce(f"swiglu masked full size G={G} M={M} I={I} K={K} seed {seed}")
     d = W.masked(seed, G, M, N, K)
     Yk, syk = gpu_masked(d["A"], d["sa"], d["B"], d["sb"], d["masked_m"], d["expected_m"])
-    compare_masked(d["A"], d["sa"], d["B"], d["sb"], d["masked_m"], Yk, syk, "masked full size",
-                   rows_per_group=2, seed=7)
+    compare_masked(d["A"], d["sa"], d["B"], d["sb"], d["masked_m"], Yk, syk, "masked full size")
 
 
 def test_moe_layer_chain():
