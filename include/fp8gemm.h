@@ -81,8 +81,10 @@ enum fp8gemm_status {
   FP8GEMM_INVALID_ARG = 1,       /* null pointer for a non-empty problem, negative size, G < 1, expected_m < 0 */
   FP8GEMM_UNSUPPORTED_SHAPE = 2, /* K % 128 != 0; contiguous layout with M % 128 != 0; sizes past 2^31 elements */
   FP8GEMM_MISALIGNED = 3,        /* A, B or D not 16-byte aligned, sa or sb not 4-byte aligned */
-  FP8GEMM_LAUNCH_FAILED = 4      /* the HIP runtime refused one of the call's own launches (an
+  FP8GEMM_LAUNCH_FAILED = 4,     /* the HIP runtime refused one of the call's own launches (an
                                     error left by an earlier HIP call is not reported) */
+  FP8GEMM_SCRATCH_EXCEEDED = 5   /* allocation-free entry point only: the call's plan needs more
+                                    than its fixed scratch (32 MB) */
 };
 
 /*
@@ -91,6 +93,28 @@ enum fp8gemm_status {
  */
 int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, const float *sb,
                                 void *D, int M, int N, int K, void *stream);
+
+/*
+ * Allocation-free form of the dense GEMM, for callers that cannot allocate
+ * device memory: code under HIP graph capture that must not call hipMalloc,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * layouts, kernels and results as gemm_fp8_1x128_128x128_bf16 (bit for bit,
+ * where that call gets a workspace); the only difference is where a split
+ * call keeps its fp32 partials: a fixed 32 MB device array of the library
+ * (one per GPU, created when the library's code is loaded on it and held
+ * until the process ends), whose address is looked up on the first call on
+ * each device.  The call allocates nothing and calls no allocating routine.
+ * Every split call of this entry point on one GPU uses the same array:
+ * calls that overlap on one GPU (on different streams, or graph replays)
+ * race on it and give wrong results; calls ordered on one stream are safe.
+ * Nothing in the array needs clearing (each call overwrites the partials it
+ * reads).  Every default plan fits 32 MB; a plan that needs more (possible
+ * only through a tuning override) returns FP8GEMM_SCRATCH_EXCEEDED before
+ * anything is launched.
+ */
+int gemm_fp8_1x128_128x128_bf16_noalloc(const void *A, const float *sa, const void *B,
+                                        const float *sb, void *D, int M, int N, int K,
+                                        void *stream);
 
 /*
  * M-axis contiguous grouped GEMM (GeekNews "성능 평가", contiguous layout:

@@ -34,7 +34,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8gemm.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "fp8gemm.h")
 
-__all__ = ["gemm_fp8_1x128_128x128_bf16", "grouped_contiguous", "grouped_masked",
+__all__ = ["gemm_fp8_1x128_128x128_bf16", "gemm_fp8_1x128_128x128_bf16_noalloc",
+           "grouped_contiguous", "grouped_masked",
            "quantize_fp8_1x128", "grouped_contiguous_swiglu_fp8", "grouped_masked_swiglu_fp8",
            "gemm_bf16_nt", "grouped_contiguous_bf16", "grouped_masked_bf16",
            "fp8gemm_status_string", "Fp8GemmError", "load_library",
@@ -59,6 +60,7 @@ def load_library():
         lib = ctypes.CDLL(LIB_PATH)
         vp, i32 = ctypes.c_void_p, ctypes.c_int
         lib.gemm_fp8_1x128_128x128_bf16.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
+        lib.gemm_fp8_1x128_128x128_bf16_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
         lib.grouped_contiguous.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
         lib.grouped_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, i32]
         lib.quantize_fp8_1x128.argtypes = [vp, vp, vp, i32, i32, vp]
@@ -69,7 +71,8 @@ def load_library():
         lib.gemm_bf16_nt.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         lib.grouped_contiguous_bf16.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
         lib.grouped_masked_bf16.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32]
-        for f in (lib.gemm_fp8_1x128_128x128_bf16, lib.grouped_contiguous, lib.grouped_masked,
+        for f in (lib.gemm_fp8_1x128_128x128_bf16, lib.gemm_fp8_1x128_128x128_bf16_noalloc,
+                  lib.grouped_contiguous, lib.grouped_masked,
                   lib.quantize_fp8_1x128, lib.grouped_contiguous_swiglu_fp8,
                   lib.grouped_masked_swiglu_fp8, lib.gemm_bf16_nt, lib.grouped_contiguous_bf16,
                   lib.grouped_masked_bf16):
@@ -143,6 +146,25 @@ def gemm_fp8_1x128_128x128_bf16(A, sa, B, sb, D=None, stream=None):
         raise TypeError("sa, sb must be float32 and D bfloat16")
     dev = _dev(A, sa, B, sb, D)
     _check(load_library().gemm_fp8_1x128_128x128_bf16(
+        _p(A), _p(sa), _p(B), _p(sb), _p(D), M, N, K, _stream(stream, dev)))
+    return D
+
+
+def gemm_fp8_1x128_128x128_bf16_noalloc(A, sa, B, sb, D, stream=None):
+    """The allocation-free form of gemm_fp8_1x128_128x128_bf16: same result,
+    split-K partials in the library's fixed device scratch, nothing allocated
+    (D must be given).  Calls that overlap on one GPU race on the scratch."""
+    A, B = _codes(A, "A"), _codes(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    _shape(B, (N, K), "B")
+    _shape(sa, (K // 128, M), "sa")
+    _shape(sb, ((N + 127) // 128, K // 128), "sb")
+    _shape(D, (M, N), "D")
+    if sa.dtype != torch.float32 or sb.dtype != torch.float32 or D.dtype != torch.bfloat16:
+        raise TypeError("sa, sb must be float32 and D bfloat16")
+    dev = _dev(A, sa, B, sb, D)
+    _check(load_library().gemm_fp8_1x128_128x128_bf16_noalloc(
         _p(A), _p(sa), _p(B), _p(sb), _p(D), M, N, K, _stream(stream, dev)))
     return D
 

@@ -1418,6 +1418,44 @@ struct WsLease {
   ~WsLease() { release(); }
 };
 
+// ---- fixed scratch of the allocation-free entry point --------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// from module load until the process ends.  Host code must not pass the
+// array's name to a kernel (on the host it names a stand-in, not device
+// memory): the address comes from hipGetSymbolAddress, once per device with
+// that device current, and is kept per device.  Every call of that entry
+// point on a GPU shares the array; it keeps the last call's partials, which
+// every call overwrites before reading (nothing in it must start at zero).
+constexpr size_t SCRATCH_FLOATS = WS_FLOATS;  // 32 MB: every default plan fits
+static __device__ __align__(256) float scratch[SCRATCH_FLOATS];
+
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[MAX_DEV];
+
+// the current device's address of `scratch`, or nullptr on a runtime error
+float *scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    // a symbol lookup, no stream operation: allowed while a stream captures
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    const bool exchanged = hipThreadExchangeStreamCaptureMode(&mode) == hipSuccess;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (exchanged) (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<float *>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, int LAYOUT, bool KSPLIT = false,
           bool ACT = false, bool BF = false>
 int launch_tile(Args a, int groups, hipStream_t stream) {
@@ -1496,8 +1534,10 @@ DecodeCfg decode_config(int M, int N, int Kb, bool bf) {
 }
 
 // BF: bf16 operands, K blocks of 64 elements (128 bytes)
+// fixed_ws: a caller-provided scratch of SCRATCH_FLOATS (the allocation-free
+// entry point); nullptr: the library workspace (WsLease)
 template <bool BF>
-int run_decode(Args a, hipStream_t stream) {
+int run_decode(Args a, hipStream_t stream, float *fixed_ws = nullptr) {
   const int Kb = (BF ? 2 * a.K : a.K) / BK;
   DecodeCfg c = decode_config(a.M, a.N, Kb, BF);
   const int bm = a.M <= 64 ? 64 : 128;
@@ -1508,7 +1548,11 @@ int run_decode(Args a, hipStream_t stream) {
   a.kb_per_split = kps;
   WsLease ws;  // held until the reduction is enqueued
   if (splits > 1) {
-    if ((size_t)splits * a.M * a.N > WS_FLOATS || !ws.acquire(stream)) {
+    const size_t need = (size_t)splits * a.M * a.N;
+    if (fixed_ws) {
+      if (need > SCRATCH_FLOATS) return FP8GEMM_SCRATCH_EXCEEDED;
+      a.ws = fixed_ws;
+    } else if (need > WS_FLOATS || !ws.acquire(stream)) {
       a.splits = 1;
       a.kb_per_split = Kb;
     } else {
@@ -1609,14 +1653,21 @@ hipError_t launch_walk(Args &a, int P, hipStream_t stream) {
 // items of the same grid, and tail_reduce_kernel adds the parts.  Without a
 // workspace the tail is not split.
 template <int WGN, int WGM, int TN, int TM, int STAGES, int NLD, bool BF = false>
-int launch_dense_large(Args a, hipStream_t stream) {
+int launch_dense_large(Args a, hipStream_t stream, float *fixed_ws = nullptr) {
   constexpr int BN = WGN * TN * 16, BM = WGM * TM * 16;
   const int tiles_m = cdiv(a.M, BM), tiles_n = cdiv(a.N, BN), T = tiles_m * tiles_n;
   const int Kb = (BF ? 2 * a.K : a.K) / BK, R = T % 256;
   int S = R > 0 && R <= 128 ? std::min(8, 256 / R) : 1;
   while (S > 1 && cdiv(Kb, S) < 4) --S;
   WsLease ws;  // held until the tail reduction is enqueued
-  if (S > 1 && ((size_t)R * S * BM * BN > WS_FLOATS || !ws.acquire(stream))) S = 1;
+  if (S > 1) {
+    const size_t need = (size_t)R * S * BM * BN;
+    if (fixed_ws) {
+      if (need > SCRATCH_FLOATS) return FP8GEMM_SCRATCH_EXCEEDED;
+    } else if (need > WS_FLOATS || !ws.acquire(stream)) {
+      S = 1;
+    }
+  }
   // more tiles than CUs: the persistent walk over the same items
   const int P = walk_workgroups();
   const bool walk = walk_enabled(BF ? 2 * a.K : a.K) && P >= 8 && T > P;
@@ -1634,7 +1685,7 @@ int launch_dense_large(Args a, hipStream_t stream) {
   a.full_tiles = T - R;
   a.tail_splits = cdiv(Kb, kb);
   a.tail_kb = kb;
-  a.ws = ws.ptr;
+  a.ws = fixed_ws ? fixed_ws : ws.ptr;
   hipError_t er;
   if (walk) {
     er = launch_walk<WGN, WGM, TN, TM, STAGES, NLD, DENSE, BF>(a, P, stream);
@@ -1686,19 +1737,19 @@ int check_common(const void *A, const float *sa, const void *B, const float *sb,
   return FP8GEMM_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, const float *sb,
-                                void *D, int M, int N, int K, void *stream) {
+// The dense call; fixed: the split-K partials go to `scratch` (the
+// allocation-free entry point) instead of the library workspace.
+int dense_fp8(const void *A, const float *sa, const void *B, const float *sb, void *D, int M, int N,
+              int K, void *stream, bool fixed) {
   const int st = check_common(A, sa, B, sb, D, M, N, K, (long long)M * K, (long long)N * K,
                               (long long)M * N);
   if (st != FP8GEMM_OK) return st < 0 ? FP8GEMM_OK : st;
+  float *fws = nullptr;
+  if (fixed && !(fws = scratch_ptr())) return FP8GEMM_LAUNCH_FAILED;
   Args a{static_cast<const uint8_t *>(A), sa, static_cast<const uint8_t *>(B), sb,
          static_cast<uint16_t *>(D), M, N, K, 1, nullptr, 0, 0, 1, K / BK, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= 128 && K <= 20480) return run_decode<false>(a, s);
+  if (M <= 128 && K <= 20480) return run_decode<false>(a, s, fws);
   if (K > 20480) return launch<128, 128, DENSE>(a, 1, s);
   // 256 weight rows x 128 activation rows, eight compute waves (two per
   // SIMD, so one wave's promotion FMAs run under the other's MFMAs) and four
@@ -1706,7 +1757,22 @@ int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, c
   // 256 tiles); FP8GEMM_LARGE=6 selects the four-compute-wave layout
   const char *e = getenv("FP8GEMM_LARGE");
   if (e && e[0] == '6') return launch_tile<2, 2, 4, 8, 3, 2, DENSE>(a, 1, s);
-  return launch_dense_large<4, 2, 4, 4, 3, 4>(a, s);
+  return launch_dense_large<4, 2, 4, 4, 3, 4>(a, s, fws);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_fp8_1x128_128x128_bf16(const void *A, const float *sa, const void *B, const float *sb,
+                                void *D, int M, int N, int K, void *stream) {
+  return dense_fp8(A, sa, B, sb, D, M, N, K, stream, false);
+}
+
+int gemm_fp8_1x128_128x128_bf16_noalloc(const void *A, const float *sa, const void *B,
+                                        const float *sb, void *D, int M, int N, int K,
+                                        void *stream) {
+  return dense_fp8(A, sa, B, sb, D, M, N, K, stream, true);
 }
 
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
@@ -1889,6 +1955,7 @@ const char *fp8gemm_status_string(int status) {
     case FP8GEMM_UNSUPPORTED_SHAPE: return "unsupported shape (K % 128 != 0, contiguous M % 128 != 0, or too large)";
     case FP8GEMM_MISALIGNED: return "misaligned pointer (A, B, D need 16 bytes; scales and indices 4)";
     case FP8GEMM_LAUNCH_FAILED: return "kernel launch failed";
+    case FP8GEMM_SCRATCH_EXCEEDED: return "the call's plan needs more than the 32 MB fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -20,7 +20,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = fg.declared_functions()
-    assert set(names) == {"gemm_fp8_1x128_128x128_bf16", "grouped_contiguous",
+    assert set(names) == {"gemm_fp8_1x128_128x128_bf16", "gemm_fp8_1x128_128x128_bf16_noalloc",
+                          "grouped_contiguous",
                           "grouped_masked", "quantize_fp8_1x128",
                           "grouped_contiguous_swiglu_fp8", "grouped_masked_swiglu_fp8",
                           "gemm_bf16_nt", "grouped_contiguous_bf16", "grouped_masked_bf16",
@@ -30,8 +31,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
-        assert fg.fp8gemm_status_string(s)
+    for s in range(6):
+        assert fg.fp8gemm_status_string(s) != "unknown status"
     assert fg.fp8gemm_status_string(99) == "unknown status"
 
 
@@ -55,6 +56,17 @@ def test_dense_validation(lib):
     # empty problems succeed without launching, even with null pointers
     assert dense(lib, A=NUL, sa=NUL, B=NUL, sb=NUL, D=NUL, M=0) == OK
     assert dense(lib, A=NUL, sa=NUL, B=NUL, sb=NUL, D=NUL, N=0) == OK
+
+
+def test_dense_noalloc_validation(lib):
+    """the allocation-free dense call validates exactly as the dense call"""
+    def call(A=P, sa=P, B=P, sb=P, D=P, M=64, N=64, K=128):
+        return lib.gemm_fp8_1x128_128x128_bf16_noalloc(A, sa, B, sb, D, M, N, K, NUL)
+    for kw, want in (({"M": -1}, INVALID), ({"A": NUL}, INVALID), ({"D": NUL}, INVALID),
+                     ({"K": 100}, SHAPE), ({"A": P_ODD}, MISALIGNED),
+                     ({"M": 1 << 20, "K": 1 << 12}, SHAPE)):
+        assert call(**kw) == want == dense(lib, **kw), kw
+    assert call(A=NUL, sa=NUL, B=NUL, sb=NUL, D=NUL, M=0) == OK
 
 
 def test_contiguous_validation(lib):
