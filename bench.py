@@ -4,18 +4,22 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
 
 A step is one pass of the hot path over one batch of the workload: one GEMM
 call per shape of the workload, inputs already resident in HBM, launched as a
-HIP graph replay (the decode regime's launch mode).  The default
-workload is the decode-shaped dense set (M in {64, 128} x (N, K) in
-{(2112,7168), (24576,1536), (7168,2048), (4096,7168)}), which is memory-bound:
-`value` is algorithmic bytes moved per second (GB/s) over the timed steps,
-counting A, B, the scales and D once per call.  Every step uses a different
-copy of the inputs (rotating sets totalling > 1 GB) so weights come from HBM,
-not from the 256 MB last-level cache.
+HIP graph replay.  With no --workload, the headline is the largest workload,
+the MoE grouped GEMM in the M-axis contiguous layout (G=4 experts x 8192 rows
+and G=8 uneven experts, 32768 rows, N=4096, K=7168), which is MFMA-bound:
+`value` is algorithmic FLOP per second (TFLOP/s) over the K timed steps.  The
+same line then carries, under `per_config`, the other workloads timed the same
+way in the same run: decode (M in {64,128}, HBM-bound, GB/s), prefill (M=4096,
+TFLOP/s) and masked (G=16, HBM-bound, GB/s).  Every step uses a different copy
+of the inputs where one copy is under 1 GB (rotating sets totalling > 1 GB) so
+weights come from HBM, not from the 256 MB last-level cache.
 
 Rank 0 prints one JSON line.  Extra fields: per-shape kernel times (HIP
 events on the launch stream around back-to-back graph replays of that
-shape's kernel), the roofline of the dominant shape's kernel, and the CPU
-oracle timed on a bounded sample of the same workload.
+shape's kernel), the roofline of the dominant shape's kernel (with the
+committed rocprofv3 trace's mean duration of the same call beside it), and
+the CPU oracle timed on a bounded sample of the same workload on every host
+core.
 """
 import argparse
 import json
@@ -169,6 +173,8 @@ WORKLOAD_TEXT = {
     "quant": "1x128 FP8 quantisation of bf16 activations, M=4096 x K in {16384,7168,1536,18432} (the prefill A operands), 1% rows x50",
 }
 MEMORY_BOUND = {"decode", "small", "masked", "quant"}
+DEFAULT_WORKLOAD = "contiguous"  # the largest configuration: the headline
+EXTRA_WORKLOADS = ("decode", "prefill", "masked")
 
 
 def main():
@@ -176,7 +182,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOAD_TEXT),
+                    help=f"time this workload only (default: {DEFAULT_WORKLOAD}, with "
+                         + ", ".join(EXTRA_WORKLOADS) + " under per_config)")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="with the default workload, skip the per_config workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -188,7 +198,7 @@ def main():
                          "profiles/<workload>.traffic.json")
     args = ap.parse_args()
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.workload)
+        summarize_profile(args.summarize_profile, args.workload or DEFAULT_WORKLOAD)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU form "
@@ -208,12 +218,54 @@ def main():
         return
 
     import moe_grouped_gemm_act_amd as fg
-    from synth import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    calls = workload_calls(args.workload)
     stream = torch.cuda.Stream(dev)
+    workload = args.workload or DEFAULT_WORKLOAD
+    head = measure(torch, fg, workload, args.steps, args.warmup, dev, stream)
+    per_config = None
+    if args.workload is None and not args.no_extra_configs:
+        per_config = {}
+        for w in EXTRA_WORKLOADS:
+            r = measure(torch, fg, w, args.steps, args.warmup, dev, stream)
+            per_config[w] = {k: r[k] for k in ("workload", "value", "unit", "ms_per_step", "frac",
+                                               "rotating_copies", "per_call", "roofline")}
+    calls = head.pop("calls")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(calls, args.cpu_seconds, head["memory_bound"])
+
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulate)" if workload == "bf16" else "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[workload], "calls": len(head["per_call"]),
+                   "rotating_copies": head["rotating_copies"], "parallelism": "none (1 GPU)"},
+        "tflops": head["tflops"],
+        "frac_fp8_peak": head["tflops"] / PEAK_FP8_TFLOPS,
+        "frac_mfma_peak": head["tflops"] / (PEAK_BF16_TFLOPS if workload == "bf16" else PEAK_FP8_TFLOPS),
+        "gbps": head["gbps"],
+        "frac_hbm_peak": head["gbps"] / PEAK_HBM_GBS,
+        "per_call": head["per_call"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if per_config is not None:
+        line["per_config"] = per_config
+    print(json.dumps(line), flush=True)
+
+
+def measure(torch, fg, workload, steps, warmup, dev, stream):
+    """Time one workload: W warm-up and K timed graph replays of its step,
+    then each call on its own; returns the figures (and the calls)."""
+    calls = workload_calls(workload)
 
     # inputs: one seeded set per call, cloned on the GPU into rotating copies
     sets, total = [], 0
@@ -232,7 +284,7 @@ def main():
     # Steps run as HIP graph replays (one graph per rotation set, all calls in
     # order), so the timed region measures the GPU, not Python launch cost.
     with torch.cuda.stream(stream):
-        for j in range(copies):  # eager first: any per-stream workspace is made outside capture
+        for j in range(copies):  # eager pass first (any library set-up happens outside capture)
             for i in range(len(calls)):
                 launch(i, j)
     stream.synchronize()
@@ -244,13 +296,13 @@ def main():
                 launch(i, j)
         step_graphs.append(g)
     with torch.cuda.stream(stream):
-        for j in range(args.warmup):
+        for j in range(warmup):
             step_graphs[j % copies].replay()
     stream.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for j in range(args.steps):
+        for j in range(steps):
             step_graphs[j % copies].replay()
     stream.synchronize()
     torch.cuda.synchronize()
@@ -259,7 +311,7 @@ def main():
     # per-call kernel duration: HIP events on the launch stream around
     # back-to-back replays of a graph holding `copies` launches of that call
     per_call = []
-    reps = max(3, min(50, args.steps // 4))
+    reps = max(3, min(50, steps // 4))
     for i, c in enumerate(calls):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
@@ -277,48 +329,40 @@ def main():
         per_call.append({"call": c.label, "avg_us": avg_s * 1e6, "GBps": c.bytes / avg_s / 1e9,
                          "TFLOPS": c.flop / avg_s / 1e12, "bytes": c.bytes, "flop": c.flop})
         del g
+    del step_graphs, sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     dom = max(per_call, key=lambda r: r["avg_us"])
     step_bytes = sum(c.bytes for c in calls)
     step_flop = sum(c.flop for c in calls)
-    memory_bound = args.workload in MEMORY_BOUND
-    gbps = step_bytes * args.steps / wall / 1e9
-    tflops = step_flop * args.steps / wall / 1e12
+    memory_bound = workload in MEMORY_BOUND
+    gbps = step_bytes * steps / wall / 1e9
+    tflops = step_flop * steps / wall / 1e12
     if memory_bound:
         roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dom["GBps"] / PEAK_HBM_GBS, "traffic": None}
     else:
-        peak = PEAK_BF16_TFLOPS if args.workload == "bf16" else PEAK_FP8_TFLOPS
+        peak = PEAK_BF16_TFLOPS if workload == "bf16" else PEAK_FP8_TFLOPS
         roof = {"bound": "mfma", "achieved": dom["TFLOPS"], "peak": peak,
                 "unit": "TFLOP/s", "frac": dom["TFLOPS"] / peak, "traffic": None}
     roof["kernel"] = dom["call"]
     roof["avg_us"] = dom["avg_us"]
-    roof["traffic"] = measured_traffic(roof["kernel"])
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(calls, args.cpu_seconds, memory_bound)
-
-    line = {
-        "metric": METRIC,
-        "value": gbps if memory_bound else tflops,
-        "unit": "GB/s" if memory_bound else "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (fp32 accumulate)" if args.workload == "bf16" else "fp8_e4m3 (fp32 accumulate, bf16 out)",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "calls": len(calls),
-                   "rotating_copies": copies, "parallelism": "none (1 GPU)"},
-        "tflops": tflops,
-        "frac_fp8_peak": tflops / PEAK_FP8_TFLOPS,
-        "frac_mfma_peak": tflops / (PEAK_BF16_TFLOPS if args.workload == "bf16" else PEAK_FP8_TFLOPS),
-        "gbps": gbps,
-        "frac_hbm_peak": gbps / PEAK_HBM_GBS,
-        "per_call": per_call,
-        "roofline": roof,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+    prof = profiled_call(dom["call"])
+    roof["traffic"] = prof and prof["traffic"]
+    if prof and prof.get("trace_avg_us"):
+        # the committed rocprofv3 kernel trace of the same call (same kernel
+        # sources): its mean duration and the fraction it gives
+        t = prof["trace_avg_us"] * 1e-6
+        units = dom["bytes"] / 1e9 if memory_bound else dom["flop"] / 1e12
+        roof["profile"] = {"source": prof["source"], "trace_avg_us": prof["trace_avg_us"],
+                           "frac": units / t / roof["peak"],
+                           "live_over_trace": dom["avg_us"] / prof["trace_avg_us"]}
+    value = gbps if memory_bound else tflops
+    return {"workload": WORKLOAD_TEXT[workload], "value": value,
+            "unit": "GB/s" if memory_bound else "TFLOP/s", "ms_per_step": wall / steps * 1e3,
+            "frac": value / (PEAK_HBM_GBS if memory_bound else roof["peak"]),
+            "tflops": tflops, "gbps": gbps, "rotating_copies": copies, "per_call": per_call,
+            "roofline": roof, "memory_bound": memory_bound, "calls": calls}
 
 
 def source_sha256():
@@ -468,7 +512,7 @@ def summarize_profile(d, workload):
         fb = st.mean(fetch[i]) * fscale
         wb = st.mean(write[i]) * wscale
         alg = kline["per_call"][i]["bytes"]
-        traffic[lab] = {"fetch_bytes": fb, "write_bytes": wb}
+        traffic[lab] = {"fetch_bytes": fb, "write_bytes": wb, "trace_avg_us": st.mean(durs)}
         if sq and i in sq:
             q = sq[i]
             busy = q["SQ_BUSY_CYCLES"] / n_arr  # per shader array: the launch's cycles
@@ -521,19 +565,42 @@ busy cycles over the traced mean duration (the clock the launch ran at, approxim
     print(md)
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch (calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE) for
-    `kernel`, from the committed profile summaries -- only when they were taken
-    on the kernel source as it is now; otherwise None."""
+def profiled_call(kernel):
+    """From the committed profile summaries, for the call `kernel`, only when
+    they were taken on the kernel sources as they are now (else None): HBM
+    bytes per launch (calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE) and the
+    kernel trace's mean launch duration."""
     import glob
     sha = source_sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.json"))):
         d = json.load(open(f))
         k = d.get("kernels", {}).get(kernel)
         if d.get("source_sha256") == sha and k:
-            return {"bytes": k["fetch_bytes"] + k["write_bytes"], "fetch_bytes": k["fetch_bytes"],
-                    "write_bytes": k["write_bytes"], "source": os.path.basename(f)}
+            return {"traffic": {"bytes": k["fetch_bytes"] + k["write_bytes"], "fetch_bytes": k["fetch_bytes"],
+                                "write_bytes": k["write_bytes"], "source": os.path.basename(f)},
+                    "trace_avg_us": k.get("trace_avg_us"), "source": os.path.basename(f)}
     return None
+
+
+def host_cpu():
+    """The host's cores this process may run on, and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    quota = None
+    try:  # cgroup v2 CPU quota, if one is set
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()
+        if q != "max":
+            quota = int(q) / int(per)
+    except (OSError, ValueError):
+        pass
+    return cores, model, quota
 
 
 def cpu_baseline(calls, budget_s, memory_bound):
@@ -543,7 +610,9 @@ def cpu_baseline(calls, budget_s, memory_bound):
     import numpy as np
 
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    cores, model, quota = host_cpu()
+    threads = max(1, min(256, cores))  # every core this process may use (the oracle's cap is 256)
+    granted = min(threads, quota) if quota else threads
     t0 = time.perf_counter()
     done, by, fl, passes = [], 0, 0.0, 0
     while True:
@@ -565,7 +634,7 @@ def cpu_baseline(calls, budget_s, memory_bound):
                 M, K = A.shape
                 N = B.shape[0]
                 left = max(0.2, budget_s - (time.perf_counter() - t0))
-                rows = max(1, min(M, int(left * 3e8 * threads / (N * K))))
+                rows = max(1, min(M, int(left * 3e8 * granted / (N * K))))
                 oracle.gemm_bf16("dense", A[:rows], B, threads=threads)
                 if passes == 0:
                     done.append(f"{rows}x{N}x{K}")
@@ -582,9 +651,9 @@ def cpu_baseline(calls, budget_s, memory_bound):
             M, K = A.shape
             N = B.shape[0]
             # whole output rows, as many as the remaining budget allows at an
-            # assumed 1e9 multiply-adds per second per thread
+            # assumed 1e9 multiply-adds per second per core actually granted
             left = max(0.2, budget_s - (time.perf_counter() - t0))
-            rows = max(1, min(M, int(left * 1e9 * threads / (N * K))))
+            rows = max(1, min(M, int(left * 1e9 * granted / (N * K))))
             sa_r = np.ascontiguousarray(sa[:, :rows])
             if c.kind.endswith("_swiglu"):  # one expert's rows through the fused oracle
                 I = N // 2
@@ -607,9 +676,10 @@ def cpu_baseline(calls, budget_s, memory_bound):
     dt = time.perf_counter() - t0
     val = by / dt / 1e9 if memory_bound else fl / dt / 1e12
     # the oracle's GEMM runs on `threads` host threads, its quantiser on one
-    cores = 1 if all(c.kind == "quant" for c in calls) else threads
-    return {"value": val, "unit": "GB/s" if memory_bound else "TFLOP/s", "cores": cores,
+    used = 1 if all(c.kind == "quant" for c in calls) else threads
+    return {"value": val, "unit": "GB/s" if memory_bound else "TFLOP/s", "cores": used,
             "kind": "oracle", "seconds": dt, "gflops": fl / dt / 1e9,
+            "host": {"cores_available": cores, "cpu_model": model, "cgroup_cpu_quota": quota},
             "sample": f"{passes} pass(es) over whole output rows of each call (first pass: "
                       + ", ".join(done) + f"), stopped after about {budget_s:.0f} s"}
 
