@@ -10,7 +10,11 @@
 // x / s correctly rounded, without a division per element: with the
 // correctly rounded reciprocal rs of s, q0 = x rs and one exact-residual
 // correction q0 + (x - q0 s) rs give the correctly rounded quotient as long
-// as the residual does not underflow.  Blocks with amax < 2^-60 are first
+// as the residual does not underflow.  This is Markstein's FMA quotient
+// correction (P. W. Markstein, "Computation of elementary functions on the
+// IBM RISC System/6000 processor", IBM J. Res. Develop. 34(1), 1990): the
+// residual x - q0 s is exact in one fused multiply-add, and one more FMA
+// with the correctly rounded reciprocal rounds the quotient correctly.  Blocks with amax < 2^-60 are first
 // scaled by 2^64 (x and s alike: the quotient does not change), which keeps
 // every element that can reach a non-zero code clear of underflow.  A scale
 // of 0 (an underflowed amax / 448) or infinity (a block holding an infinity)
