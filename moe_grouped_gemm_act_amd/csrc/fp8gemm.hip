@@ -754,6 +754,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // a wave whose activation rows all lie past the valid ones (masked rows,
+  // or past M) has nothing to compute: it only takes the barriers
+  const bool idle = m0 + wm * TM * 16 >= mvalid;
   if constexpr (BF) {
     for (int t0 = 0; t0 < nk; t0 += STAGES) {
 #pragma unroll
@@ -763,7 +766,7 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // block t is in slot u
         asm volatile("" ::: "memory");
-        bf16_kblock<TN, TM, BM>(lds[u], wn, wm, fr, fg, acc);
+        if (!idle) bf16_kblock<TN, TM, BM>(lds[u], wn, wm, fr, fg, acc);
       }
     }
   } else {
@@ -792,8 +795,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
         // addresses in registers through the loop
         int so = u * SLOT;
         if (ACT) asm volatile("" : "+s"(so));
-        fp8_kblock<WGN, TN, TM, BM, TWOB>(&lds[0][0] + so, s_sb[hsb][t], s_sb[TWOB ? 1 : hsb][t],
-                                          himask, wn, wm, fr, fg, acc, ring, sc_last);
+        if (!idle)
+          fp8_kblock<WGN, TN, TM, BM, TWOB>(&lds[0][0] + so, s_sb[hsb][t], s_sb[TWOB ? 1 : hsb][t],
+                                            himask, wn, wm, fr, fg, acc, ring, sc_last);
       }
     }
     fp8_flush<TN, TM, TWOB>(acc, ring, sc_last, himask);
@@ -1099,12 +1103,14 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // all of this wave's activation rows past the valid ones: barriers only
+    const bool idle = it.m0 + wm * TM * 16 >= it.mvalid;
     if constexpr (BF) {
       for (int t = 0; t < it.nk; ++t) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();  // this item's block t is in slot cs
         asm volatile("" ::: "memory");
-        bf16_kblock<TN, TM, BM>(&lds[0][0] + cs * SLOT, wn, wm, fr, fg, acc);
+        if (!idle) bf16_kblock<TN, TM, BM>(&lds[0][0] + cs * SLOT, wn, wm, fr, fg, acc);
         cs = cs + 1 == STAGES ? 0 : cs + 1;
       }
     } else {
@@ -1118,8 +1124,9 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
         asm volatile("" ::: "memory");
         const uint8_t *sl = &lds[0][0] + cs * SLOT;
         const float *sbs = reinterpret_cast<const float *>(sl + SBOFF);
-        fp8_kblock<WGN, TN, TM, BM, ACT>(sl, sbs[hsb], sbs[ACT ? 1 : hsb], ACT ? 0xCu : 0u, wn, wm, fr,
-                                         fg, acc, ring, sc_last);
+        if (!idle)
+          fp8_kblock<WGN, TN, TM, BM, ACT>(sl, sbs[hsb], sbs[ACT ? 1 : hsb], ACT ? 0xCu : 0u, wn, wm,
+                                           fr, fg, acc, ring, sc_last);
         cs = cs + 1 == STAGES ? 0 : cs + 1;
       }
       fp8_flush<TN, TM, ACT>(acc, ring, sc_last, ACT ? 0xCu : 0u);
@@ -1810,24 +1817,42 @@ int grouped_masked(const void *A, const float *sa, const void *B, const float *s
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K > 20480) return launch<64, 128, MASKED>(a, G, s);
   // measured on MI355X (G = 16, 256-row capacity, counts ~ U[0, 256]):
-  // 128 weight rows by 128 activation rows, eight compute waves (2-3% over
-  // four: two per SIMD overlap promotion FMAs with MFMAs), four loader
-  // waves, four slots;
-  // 64-row activation tiles when the hint says counts are small; for short K
-  // (K = 2048: 20% faster, but 9% slower at K = 7168) 256 weight rows, which
-  // halve the activation re-reads and the tiles' fixed costs
+  // eight compute waves (two per SIMD overlap promotion FMAs with MFMAs),
+  // four loader waves; 64-row activation tiles when the hint says counts are
+  // small; for short K 256 weight rows, which halve the activation re-reads
+  // and the tiles' fixed costs
   if (expected_m <= 64) return launch_tile<1, 4, 8, 1, 4, 4, MASKED>(a, G, s);
-  // the persistent walk over the live tiles (up to WALK_MAXG experts)
   const int P = walk_workgroups();
-  const bool walk = walk_enabled(K, true) && P >= 8 && G <= WALK_MAXG;
+  const char *we = getenv("FP8GEMM_WALK"), *mt = getenv("FP8GEMM_MASKED");
+  // the persistent walk over the live tiles (up to WALK_MAXG experts, rows
+  // of at most 8 KB); FP8GEMM_WALK=0 turns it off, =2 also walks K <= 4096
+  const bool walk = !(we && we[0] == '0') && P >= 8 && G <= WALK_MAXG && K <= 8192;
+  const bool walk_all = walk && we && we[0] == '2';
+  if (K > 4096 && !(mt && mt[0] == '0')) {
+    // 256 activation rows (a whole expert of a 256-row capacity) by 128
+    // weight rows, walked over the live tiles: each expert's weight tile is
+    // streamed once, not once per 128-row activation tile, and compute waves
+    // whose 64 rows lie past masked_m skip their MFMAs (G = 16 x 256 x 4096
+    // x 7168: 123 us, against 126 us for 128-row activation tiles; the walk
+    // and one workgroup per tile measure the same)
+    if (!walk) return launch_tile<2, 4, 4, 4, 3, 4, MASKED>(a, G, s);
+    a.tiles_m = cdiv(M, 256);
+    a.tiles_n = cdiv(N, 128);
+    return launch_walk<2, 4, 4, 4, 3, 4, MASKED, false>(a, P, s) == hipSuccess ? FP8GEMM_OK
+                                                                               : FP8GEMM_LAUNCH_FAILED;
+  }
   if (K <= 4096) {
-    if (!walk) return launch_tile<4, 2, 4, 4, 3, 4, MASKED>(a, G, s);
+    // 256 weight rows by 128 activation rows, one workgroup per (tile,
+    // expert), dead tiles exiting at once (the walk measured 2-4% slower at
+    // 16 x 256 x 7168 x 2048)
+    if (!walk_all) return launch_tile<4, 2, 4, 4, 3, 4, MASKED>(a, G, s);
     a.tiles_m = cdiv(M, 128);
     a.tiles_n = cdiv(N, 256);
     return launch_walk<4, 2, 4, 4, 3, 4, MASKED, false>(a, P, s) == hipSuccess ? FP8GEMM_OK
                                                                                : FP8GEMM_LAUNCH_FAILED;
   }
-  if (!walk) return launch_tile<2, 4, 4, 2, 4, 4, MASKED>(a, G, s);
+  // K > 4096 with FP8GEMM_MASKED=0 (tuning override): 128 x 128 tiles
+  if (!walk_all) return launch_tile<2, 4, 4, 2, 4, 4, MASKED>(a, G, s);
   a.tiles_m = cdiv(M, 128);
   a.tiles_n = cdiv(N, 128);
   return launch_walk<2, 4, 4, 2, 4, 4, MASKED, false>(a, P, s) == hipSuccess ? FP8GEMM_OK

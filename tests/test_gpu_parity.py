@@ -432,14 +432,19 @@ def test_masked_count_sweep_and_hint():
         outs.append(out)
 
 
-@pytest.mark.parametrize("walk", ["2", "default"])
+@pytest.mark.parametrize("walk", ["2", "default", "walk0", "tile128"])
 @pytest.mark.parametrize("G,M,N,K", [(70, 130, 260, 256),    # more experts than one wave scans at once
-                                     (12, 130, 300, 4224)])  # K > 4096: the 128 x 128 tile
+                                     (12, 130, 300, 4224)])  # K > 4096: 256-row activation tiles
 def test_masked_persistent_walk_full(G, M, N, K, walk, monkeypatch):
-    """The walk over the live tiles only (FP8GEMM_WALK=2; counts clamped to
-    [0, M], zero, past M, one row past a tile) and the default, one workgroup
-    per (tile, expert)."""
-    if walk != "default":
+    """Counts clamped to [0, M], zero, past M, one row past a tile, through
+    the walk over the live tiles (default at K > 4096, FP8GEMM_WALK=2 for
+    every K), one workgroup per (tile, expert) (default at K <= 4096,
+    FP8GEMM_WALK=0) and 128-row activation tiles (FP8GEMM_MASKED=0)."""
+    if walk == "walk0":
+        monkeypatch.setenv("FP8GEMM_WALK", "0")
+    elif walk == "tile128":
+        monkeypatch.setenv("FP8GEMM_MASKED", "0")
+    elif walk != "default":
         monkeypatch.setenv("FP8GEMM_WALK", walk)
     seed = 5300 + G
     d = W.masked(seed, G, M, N, K)
@@ -485,15 +490,22 @@ def masked_workload(case):
     return d, ref
 
 
-@pytest.mark.parametrize("walk", ["default", "2"])
+MASKED_VARIANTS = {"default": {}, "walk0": {"FP8GEMM_WALK": "0"}, "walk2": {"FP8GEMM_WALK": "2"},
+                   "tile128": {"FP8GEMM_MASKED": "0"}, "tile128walk": {"FP8GEMM_MASKED": "0", "FP8GEMM_WALK": "2"}}
+
+
+@pytest.mark.parametrize("variant", sorted(MASKED_VARIANTS))
 @pytest.mark.parametrize("case", range(len(W.MASKED_CASES)))
-def test_masked_workload_full(case, walk, monkeypatch):
-    """The masked workload shapes, one workgroup per (tile, expert) and, with
-    FP8GEMM_WALK=2, the persistent walk over the live tiles."""
-    if walk != "default":
-        monkeypatch.setenv("FP8GEMM_WALK", walk)
+def test_masked_workload_full(case, variant, monkeypatch):
+    """The masked workload shapes through every masked instance: the default
+    (K = 7168: 256-row activation tiles walked over the live tiles; K = 2048:
+    one workgroup per tile and expert), the walk turned off (FP8GEMM_WALK=0)
+    or on for every K (=2), and 128-row activation tiles (FP8GEMM_MASKED=0),
+    one workgroup per tile or walked."""
+    for k, v in MASKED_VARIANTS[variant].items():
+        monkeypatch.setenv(k, v)
     G, M, N, K = W.MASKED_CASES[case]
-    announce(f"masked walk={walk} G={G} {M}x{N}x{K} seed {5000 + case}")
+    announce(f"masked {variant} G={G} {M}x{N}x{K} seed {5000 + case}")
     d, ref = masked_workload(case)
     out = gpu_masked(d)
     mm = d["masked_m"]
