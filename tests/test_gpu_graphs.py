@@ -68,6 +68,18 @@ def test_graph_masked_fp8():
                         lambda: fg.grouped_masked(A, sa, B, sb, mm, 96, D), [D])
 
 
+def test_graph_masked_fp8_walk():
+    """K > 4096: the masked call walks its live tiles (256-row activation
+    tiles, expert offsets built from masked_m on the device) by default"""
+    d = W.masked(8812, 5, 256, 384, 4352)
+    d["masked_m"] = np.array([256, 0, 129, 7, 300], np.int32)
+    A, sa, B, sb = (to_gpu(d[k]) for k in ("A", "sa", "B", "sb"))
+    mm = to_gpu(d["masked_m"])
+    D = torch.empty((5, 256, 384), dtype=torch.bfloat16, device="cuda")
+    replay_equals_eager("masked walk 5x256x384x4352",
+                        lambda: fg.grouped_masked(A, sa, B, sb, mm, 128, D), [D])
+
+
 def test_graph_swiglu_contiguous_and_masked():
     G, rows, I, K = 3, 768, 256, 1024
     idx, _ = synth.contiguous_indices(8823, G, rows, False)
