@@ -366,13 +366,17 @@ def measure(torch, fg, workload, steps, warmup, dev, stream):
 
 
 def source_sha256():
-    """sha256 over the library's kernel sources (csrc/*.hip then csrc/*.h, in name order)."""
+    """sha256 over what the library's code is made from: the kernel sources
+    (csrc/*.hip then csrc/*.h, in name order), then the build script with its
+    compiler flags."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "moe_grouped_gemm_act_amd", "csrc")
+    pkg = os.path.join(ROOT, "moe_grouped_gemm_act_amd")
+    csrc = os.path.join(pkg, "csrc")
     for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(open(f, "rb").read())
+    h.update(open(os.path.join(pkg, "build.py"), "rb").read())
     return h.hexdigest()
 
 
@@ -527,8 +531,8 @@ def summarize_profile(d, workload):
     md = f"""# rocprofv3: {w} workload
 
 Workload: {WORKLOAD_TEXT[w]}; seeded synthetic inputs, {kline['config']['rotating_copies']} rotating
-input copies (> 1 GB) so the weights come from HBM.  Kernel source sha256 `{sha}`
-(moe_grouped_gemm_act_amd/csrc/*.hip, in name order).
+input copies (> 1 GB) so the weights come from HBM.  Library sha256 `{sha}`
+(moe_grouped_gemm_act_amd/csrc/*.hip, then *.h, in name order, then build.py with its flags).
 
 Commands (repository root, one MI355X, after `cd /tmp && export TMPDIR=/tmp`), then
 `python3 bench.py --workload {w} --summarize-profile gpurun_out/prof` to write this file:
