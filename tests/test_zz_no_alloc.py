@@ -77,3 +77,33 @@ def test_noalloc_rejects_a_plan_past_the_scratch(monkeypatch):
     fg.gemm_fp8_1x128_128x128_bf16(*t, D)
     torch.cuda.synchronize()
     assert_close(bits(D), oracle.gemm(d["A"], d["sa"], d["B"], d["sb"]), "regular call, override unsplit")
+
+
+def test_noalloc_under_graph_capture():
+    """The allocation-free call captured into a graph (no allocation during
+    the capture): every replay, with eager calls of the same shape in
+    between, equals the regular call's result bit for bit."""
+    M, N, K = 128, 4096, 7168
+    d, t = inputs(9530, M, N, K)
+    R = sentinel_out((M, N))
+    fg.gemm_fp8_1x128_128x128_bf16(*t, R)
+    torch.cuda.synchronize()
+    ref = bits(R)
+    s = torch.cuda.Stream()
+    D = sentinel_out((M, N))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    announce("noalloc under graph capture 128x4096x7168")
+    with torch.cuda.graph(g, stream=s):
+        fg.gemm_fp8_1x128_128x128_bf16_noalloc(*t, D)
+    E = sentinel_out((M, N))
+    for r in range(3):
+        D.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        assert (bits(D) == ref).all(), f"replay {r}"
+        fg.gemm_fp8_1x128_128x128_bf16_noalloc(*t, E)  # eager, ordered after the replay
+        torch.cuda.synchronize()
+        assert (bits(E) == ref).all()
