@@ -18,9 +18,9 @@
 // of sa.  (One wave per row with 1 KB row reads measured slower.)  The grid
 // runs K blocks fastest, so the workgroups in flight read whole rows
 // together: 9-20% faster than row groups fastest at K = 16384, 18432 and
-// 1536 (8% slower at K = 7168).  Codes and scales go out with non-temporal
-// stores, since this kernel never reads them back: 13% faster at K = 16384,
-// about 1% at 18432, 3% slower at 7168.
+// 1536 (8% slower at K = 7168).  Codes and scales go out with plain stores:
+// the GEMM reads them next, and the quantise-then-GEMM pair measured the same
+// or faster with them than with non-temporal stores.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -77,9 +77,12 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *X, uint8_t *
                       qd.quotient(x[4 * i + 3]), x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
   if (live) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(A + (size_t)m * K + kb * 128 + q * 32);
-    __builtin_nontemporal_store(u32x4{c[0], c[1], c[2], c[3]}, dst);
-    __builtin_nontemporal_store(u32x4{c[4], c[5], c[6], c[7]}, dst + 1);
-    if (q == 0) __builtin_nontemporal_store(s, sa + (size_t)kb * M + m);
+    // plain stores: the GEMM that follows reads these codes and scales (the
+    // quantise-then-GEMM pair measured the same or faster than with
+    // non-temporal stores)
+    dst[0] = u32x4{c[0], c[1], c[2], c[3]};
+    dst[1] = u32x4{c[4], c[5], c[6], c[7]};
+    if (q == 0) sa[(size_t)kb * M + m] = s;
   }
 }
 
