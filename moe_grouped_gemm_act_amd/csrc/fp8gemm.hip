@@ -116,6 +116,16 @@ __device__ __forceinline__ bf16x8 bf_half(const v8i &v, int h) {
   return __builtin_bit_cast(bf16x8, x);
 }
 
+// a fragment from its two 16-byte halves' addresses
+__device__ __forceinline__ v8i frag_at(const uint8_t *plo, const uint8_t *phi) {
+  const u32x4 lo = *reinterpret_cast<const u32x4 *>(plo);
+  const u32x4 hi = *reinterpret_cast<const u32x4 *>(phi);
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
 __device__ __forceinline__ v8i frag(const uint8_t *row_ptr, int row, int g) {
   u32x4 lo = *reinterpret_cast<const u32x4 *>(row_ptr + chunk_pos(g, row));
   u32x4 hi = *reinterpret_cast<const u32x4 *>(row_ptr + chunk_pos(g + 4, row));
@@ -375,35 +385,35 @@ __device__ __forceinline__ void fp8_kblock(const uint8_t *sl, float sbv, float s
   constexpr int RING = ring_size<TN, TM>(), LAG = RING / 2;
   constexpr int ROWS = BM + WGN * TN * 16;
   static_assert((TN * TM) % RING == 0 && LAG < RING && LAG <= TN, "product ring");
-  const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK);
+  // Every fragment row is 16 q + fr, so its swizzle depends on fr alone: two
+  // per-lane offsets (one per 16-byte half) locate every fragment of the
+  // wave, and a fragment's row group is a constant offset from them (four
+  // address adds per block; the rest are immediate offsets).
+  const int lo = fr * BK + chunk_pos(fg, fr), hi = fr * BK + chunk_pos(fg + 4, fr);
+  const uint8_t *pa = sl + wm * TM * 16 * BK, *pb = sl + (BM + wn * TN * 16) * BK;
+  const uint8_t *palo = pa + lo, *pahi = pa + hi, *pblo = pb + lo, *pbhi = pb + hi;
+  const float *ssl = reinterpret_cast<const float *>(sl + ROWS * BK) + wm * TM * 16 + fr;
   v8i bfr[TN], afr[2];
   float scb[TM], sch[TM];  // activation scale times the weight scale sbv, and times sbv_hi
   constexpr int B0 = WGN > 1 && TN > 2 ? 2 : TN;
+  constexpr int G = 16 * BK;  // bytes per 16-row group
 #pragma unroll
-  for (int i = 0; i < B0; ++i) {
-    const int row = BM + (wn * TN + i) * 16 + fr;
-    bfr[i] = frag(sl + row * BK, row, fg);
-  }
-  {
-    const int row = wm * TM * 16 + fr;
-    afr[0] = frag(sl + row * BK, row, fg);
-    scb[0] = ssl[row] * sbv;
-    sch[0] = TWOB ? ssl[row] * sbv_hi : scb[0];
-  }
+  for (int i = 0; i < B0; ++i) bfr[i] = frag_at(pblo + i * G, pbhi + i * G);
+  afr[0] = frag_at(palo, pahi);
+  scb[0] = ssl[0] * sbv;
+  sch[0] = TWOB ? ssl[0] * sbv_hi : scb[0];
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     if (j + 1 < TM) {
-      const int row = (wm * TM + j + 1) * 16 + fr;
-      afr[(j + 1) & 1] = frag(sl + row * BK, row, fg);
-      scb[j + 1] = ssl[row] * sbv;
-      sch[j + 1] = TWOB ? ssl[row] * sbv_hi : scb[j + 1];
+      afr[(j + 1) & 1] = frag_at(palo + (j + 1) * G, pahi + (j + 1) * G);
+      scb[j + 1] = ssl[(j + 1) * 16] * sbv;
+      sch[j + 1] = TWOB ? ssl[(j + 1) * 16] * sbv_hi : scb[j + 1];
     }
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       if (j == 0 && i + B0 < TN) {
         asm volatile("" ::: "memory");  // keeps the read after the MFMAs before it
-        const int row = BM + (wn * TN + i + B0) * 16 + fr;
-        bfr[i + B0] = frag(sl + row * BK, row, fg);
+        bfr[i + B0] = frag_at(pblo + (i + B0) * G, pbhi + (i + B0) * G);
       }
       const int k = j * TN + i;
       ring[k % RING] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
