@@ -897,9 +897,12 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES][SLOT];
   __shared__ int s_grp[LAYOUT == CONTIG ? WALK_MAXIT : 1];
   __shared__ float s_rmax[ACT ? 4 * BM : 1];  // ACT: row maxima of y per wave column
-  // masked: items before expert g's (s_pre[g]) and its valid rows (s_mv[g])
+  // masked: the experts in list order (s_perm[r]: the expert at position
+  // r), the items before position r (s_pre[r]) and expert g's valid rows
+  // (s_mv[g])
   __shared__ int s_pre[LAYOUT == MASKED ? WALK_MAXG + 1 : 1];
   __shared__ int s_mv[LAYOUT == MASKED ? WALK_MAXG : 1];
+  __shared__ int s_perm[LAYOUT == MASKED ? WALK_MAXG : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -907,25 +910,48 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
   const int RB = BF ? 2 * K : K, Kb = RB / BK;
   if (LAYOUT == MASKED) {
     // the live tiles: expert g has ceil(min(max(masked_m[g], 0), M) / BM)
-    // activation tiles by tiles_n weight tiles; a wave-wide prefix sum over
-    // the experts, 64 at a time, gives each expert's first item
+    // activation tiles by tiles_n weight tiles.  Up to 64 experts are listed
+    // heaviest, lightest, second heaviest, second lightest, ... (by valid
+    // rows; ties by index), so each XCD's run of the list (below) pairs a
+    // heavily loaded expert with a lightly loaded one instead of taking
+    // neighbours in index order; more experts keep index order.  A
+    // wave-wide prefix sum over the list, 64 at a time, gives each
+    // position's first item.
     if (wave == 0) {
       const int lane = tid & 63;
-      int carry = 0;
+      const bool pair = a.G <= 64;
       for (int base = 0; base < a.G; base += 64) {
         const int g = base + lane;
-        int c = 0;
+        int mv = -1;
         if (g < a.G) {
-          const int v = a.idx[g], mv = v < 0 ? 0 : (v > M ? M : v);
+          const int v = a.idx[g];
+          mv = v < 0 ? 0 : (v > M ? M : v);
           s_mv[g] = mv;
-          c = (mv + BM - 1) / BM * a.tiles_n;
         }
+        int pos = g;
+        if (pair) {
+          int rank = 0;
+          for (int h = 0; h < a.G; ++h) {
+            const int mh = __shfl(mv, h, 64);
+            rank += (mh > mv || (mh == mv && h < g)) ? 1 : 0;
+          }
+          pos = rank < (a.G + 1) / 2 ? 2 * rank : 2 * (a.G - 1 - rank) + 1;
+        }
+        if (g < a.G) s_perm[pos] = g;
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // s_perm and s_mv written before this wave reads them
+      __builtin_amdgcn_wave_barrier();
+      int carry = 0;
+      for (int base = 0; base < a.G; base += 64) {
+        const int r = base + lane;
+        int c = 0;
+        if (r < a.G) c = (s_mv[s_perm[r]] + BM - 1) / BM * a.tiles_n;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           const int y = __shfl_up(c, d, 64);
           if (lane >= d) c += y;
         }
-        if (g < a.G) s_pre[g + 1] = carry + c;
+        if (r < a.G) s_pre[r + 1] = carry + c;
         carry += __shfl(c, 63, 64);
       }
       if (lane == 0) s_pre[0] = 0;
@@ -963,15 +989,16 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void walk_kernel(Args a) {
     it.g = 0;
     it.mvalid = M;
     if (LAYOUT == MASKED) {
-      // the expert holding live tile `tile`: the last g with s_pre[g] <= tile
+      // the list position holding live tile `tile`: the last r with
+      // s_pre[r] <= tile; its expert
       int lo = 0, hi = a.G - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_pre[mid] <= tile) lo = mid;
         else hi = mid - 1;
       }
-      it.g = lo;
-      it.mvalid = s_mv[lo];
+      it.g = s_perm[lo];
+      it.mvalid = s_mv[it.g];
       tiles_m = (s_pre[lo + 1] - s_pre[lo]) / a.tiles_n;
       tile -= s_pre[lo];
     }

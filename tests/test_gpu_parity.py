@@ -434,11 +434,14 @@ def test_masked_count_sweep_and_hint():
 
 @pytest.mark.parametrize("walk", ["2", "default", "walk0", "tile128"])
 @pytest.mark.parametrize("G,M,N,K", [(70, 130, 260, 256),    # more experts than one wave scans at once
+                                     (64, 130, 260, 256),    # the most experts the walk lists by load
+                                     (65, 130, 260, 256),    # one more: index order
                                      (12, 130, 300, 4224)])  # K > 4096: 256-row activation tiles
 def test_masked_persistent_walk_full(G, M, N, K, walk, monkeypatch):
-    """Counts clamped to [0, M], zero, past M, one row past a tile, through
-    the walk over the live tiles (default at K > 4096, FP8GEMM_WALK=2 for
-    every K), one workgroup per (tile, expert) (default at K <= 4096,
+    """Counts clamped to [0, M], zero, past M, one row past a tile, a run of
+    equal counts (the walk's load order breaks ties by index), through the
+    walk over the live tiles (default at K > 4096, FP8GEMM_WALK=2 for every
+    K), one workgroup per (tile, expert) (default at K <= 4096,
     FP8GEMM_WALK=0) and 128-row activation tiles (FP8GEMM_MASKED=0)."""
     if walk == "walk0":
         monkeypatch.setenv("FP8GEMM_WALK", "0")
@@ -450,6 +453,7 @@ def test_masked_persistent_walk_full(G, M, N, K, walk, monkeypatch):
     d = W.masked(seed, G, M, N, K)
     counts = np.random.default_rng(seed).integers(-5, M + 10, G).astype(np.int32)
     counts[:4] = [0, M, 129, M + 7]
+    counts[4:9] = 77
     d["masked_m"] = counts
     announce(f"walk {walk} masked G={G} {M}x{N}x{K} seed {seed}")
     out = gpu_masked(d, expected_m=128)
