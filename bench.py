@@ -429,6 +429,18 @@ def _call_of_dispatches(n, line):
     return [i % nc if i < head else (i - head) // ((reps + 1) * copies) for i in range(n)]
 
 
+def _timed_per_call(n, line):
+    """For each library dispatch of a bench run (the order of
+    _call_of_dispatches): whether it belongs to the timed replays of the
+    per-call phase, the launches the bench's own per-call figure covers (not
+    the first replay of each call's graph, nor the step replays, which
+    include the clock's settling after start-up)."""
+    nc, copies = len(line["per_call"]), line["config"]["rotating_copies"]
+    reps = max(3, min(50, line["steps"] // 4))
+    head = nc * (copies + line["warmup"] + line["steps"])
+    return [i >= head and (i - head) % ((reps + 1) * copies) >= copies for i in range(n)]
+
+
 def _last_json(path):
     for ln in reversed(open(path).read().splitlines()):
         if ln.startswith("{"):
@@ -453,6 +465,7 @@ def summarize_profile(d, workload):
                           key=lambda r: int(r["Dispatch_Id"])))
     kline = _last_json(os.path.join(d, w, "kt.log"))
     kcall = _call_of_dispatches(len(kt), kline)
+    ktimed = _timed_per_call(len(kt), kline)
     labels = [c["call"] for c in kline["per_call"]]
 
     def counter(sub):
@@ -505,7 +518,11 @@ def summarize_profile(d, workload):
     for i, lab in enumerate(labels):
         grps = [g for g, c in zip(kt, kcall) if c == i]
         # a launch's time: its kernels' durations (a split call's reduction included)
-        durs = [sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000 for r in g) for g in grps]
+        def dur(g):
+            return sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000 for r in g)
+        durs = [dur(g) for g in grps]
+        # the launches the bench's per-call figure times, traced
+        timed = [dur(g) for g, c, t in zip(kt, kcall, ktimed) if c == i and t]
         r0 = grps[0][0]
         names = []
         for r in grps[0]:
@@ -516,7 +533,8 @@ def summarize_profile(d, workload):
         fb = st.mean(fetch[i]) * fscale
         wb = st.mean(write[i]) * wscale
         alg = kline["per_call"][i]["bytes"]
-        traffic[lab] = {"fetch_bytes": fb, "write_bytes": wb, "trace_avg_us": st.mean(durs)}
+        traffic[lab] = {"fetch_bytes": fb, "write_bytes": wb, "trace_avg_us": st.mean(timed),
+                        "trace_all_avg_us": st.mean(durs)}
         if sq and i in sq:
             q = sq[i]
             busy = q["SQ_BUSY_CYCLES"] / n_arr  # per shader array: the launch's cycles
@@ -524,7 +542,8 @@ def summarize_profile(d, workload):
                             f"{q['SQ_LDS_BANK_CONFLICT'] / max(q['SQ_LDS_IDX_ACTIVE'], 1):.3f} | "
                             f"{busy / (st.mean(durs) * 1e3):.2f} |")
         table.append(f"| {lab} | `{name}` | {grid[0]},{grid[1]} | {len(durs)} | {st.mean(durs):.2f} | "
-                     f"{st.median(durs):.2f} | {min(durs):.2f} | {kline['per_call'][i]['avg_us']:.2f} | "
+                     f"{st.median(durs):.2f} | {min(durs):.2f} | {st.mean(timed):.2f} | "
+                     f"{kline['per_call'][i]['avg_us']:.2f} | "
                      f"{fb / 1e6:.2f} | {wb / 1e6:.2f} | {alg / 1e6:.2f} | {(fb + wb) / alg:.2f} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     cmds = "\n".join(f"    {c}" for _, c in profile_commands(w))
@@ -540,14 +559,16 @@ Commands (repository root, one MI355X, after `cd /tmp && export TMPDIR=/tmp`), t
 {cmds}
 
 Per call: kernel trace durations (all launches of that call in the traced bench run; a
-split-K or tail-split call's launch is its tile kernel plus the reduction kernel, durations added), the
-bench's own HIP-event average for the same call in that run (launch gaps included, and
-stretched by the tracer), and HBM bytes per launch from the two counter runs, scaled by the
-copy calibration below; grid is the first kernel's.  "ratio" = measured HBM bytes /
-algorithmic bytes (A, B, scales and D once each).
+split-K or tail-split call's launch is its tile kernel plus the reduction kernel, durations added);
+"timed avg us": the mean over the traced launches that the bench's per-call figure times (its
+graph replays after the first, past the start-up phase in which the clock settles), the
+duration `bench.py` quotes beside its live figure; the bench's own HIP-event average for the
+same call in that run (launch gaps included, and stretched by the tracer); and HBM bytes per
+launch from the two counter runs, scaled by the copy calibration below; grid is the first
+kernel's.  "ratio" = measured HBM bytes / algorithmic bytes (A, B, scales and D once each).
 
-| call | kernel | grid (x,y) | launches | avg us | median us | min us | bench avg us | FETCH (MB) | WRITE (MB) | algorithmic (MB) | ratio |
-|---|---|---|---|---|---|---|---|---|---|---|---|
+| call | kernel | grid (x,y) | launches | avg us | median us | min us | timed avg us | bench avg us | FETCH (MB) | WRITE (MB) | algorithmic (MB) | ratio |
+|---|---|---|---|---|---|---|---|---|---|---|---|---|
 """ + "\n".join(table) + f"""
 
 Calibration: a 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE {fkib:.0f} KiB and
