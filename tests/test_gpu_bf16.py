@@ -115,6 +115,26 @@ def test_dense_k_zero_and_empty():
                     torch.empty((5, 64), dtype=torch.bfloat16, device="cuda"), E)
 
 
+def test_grouped_k_zero():
+    """K = 0 in both grouped layouts: valid rows are empty sums (zero), the
+    others keep their sentinel"""
+    G, N = 3, 130
+    idx = np.full(128 * 2, -1, np.int32)
+    idx[:90] = 2
+    idx[128:200] = 0
+    idx[200:210] = 5  # out of range
+    announce("bf16 contiguous K=0")
+    got = gpu_contig(np.zeros((idx.size, 0), np.uint16), np.zeros((G, N, 0), np.uint16), idx)
+    valid = (idx >= 0) & (idx < G)
+    assert (got[valid] == 0).all() and (got[~valid] == SENTINEL).all()
+    mm = np.array([0, 77, 300], np.int32)
+    M = 130
+    announce("bf16 masked K=0")
+    got = gpu_masked(np.zeros((G, M, 0), np.uint16), np.zeros((G, N, 0), np.uint16), mm, 64)
+    live = np.arange(M)[None, :] < np.clip(mm, 0, M)[:, None]
+    assert (got[live] == 0).all() and (got[~live] == SENTINEL).all()
+
+
 def test_dense_prefill_shape_full():
     M, N, K = 4096, 2112, 7168
     announce(f"bf16 dense {M}x{N}x{K}")

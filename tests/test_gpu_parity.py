@@ -114,6 +114,44 @@ def test_dense_zero_k_writes_zeros():
     assert (f32(gpu_dense(d)) == 0).all()
 
 
+@pytest.mark.parametrize("walk", ["default", "0"])
+def test_grouped_zero_k_writes_zeros(walk, monkeypatch):
+    """K = 0 in both grouped layouts: every valid row is an empty sum (zero);
+    padding, out-of-range and masked rows keep their sentinel; null operand
+    pointers are allowed (nothing is read)"""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    G, N = 3, 200
+    idx = np.full(128 * 3, -1, np.int32)
+    idx[:100] = 1
+    idx[128:256] = 2
+    idx[256:300] = 7  # out of range
+    M = idx.size
+    D = sentinel_out((M, N))
+    announce(f"contiguous K=0 walk={walk}")
+    idx_d = to_gpu(idx)  # held until the call has run
+    st = fg.load_library().grouped_contiguous(None, None, None, None, D.data_ptr(), M, N, 0, G, None,
+                                              idx_d.data_ptr())
+    torch.cuda.synchronize()
+    assert st == 0, fg.fp8gemm_status_string(st)
+    out = f32(bits(D))
+    valid = (idx >= 0) & (idx < G)
+    assert (out[valid] == 0).all()
+    assert (bits(D)[~valid] == SENTINEL).all()
+    mm = np.array([0, 77, 200], np.int32)
+    Mm = 130
+    Dm = sentinel_out((G, Mm, N))
+    announce(f"masked K=0 walk={walk}")
+    mm_d = to_gpu(mm)
+    st = fg.load_library().grouped_masked(None, None, None, None, Dm.data_ptr(), Mm, N, 0, G, None,
+                                          mm_d.data_ptr(), 64)
+    torch.cuda.synchronize()
+    assert st == 0, fg.fp8gemm_status_string(st)
+    live = np.arange(Mm)[None, :] < np.clip(mm, 0, Mm)[:, None]
+    assert (f32(bits(Dm))[live] == 0).all()
+    assert (bits(Dm)[~live] == SENTINEL).all()
+
+
 def test_dense_nan_propagates():
     rng = np.random.default_rng(23)
     d = W.dense(1201, 96, 160, 256)
