@@ -94,8 +94,9 @@ struct Args {
 // of bank conflicts on gfx950 (measured with the SQ_LDS_BANK_CONFLICT
 // counter: zero, against half of all LDS cycles for a key that separates
 // only rows 8 apart).  It depends on r mod 16 only, so every 16-row fragment
-// of a tile has the same per-lane pattern and the compiler can address all
-// of them from one base with immediate offsets.
+// of a tile has the same per-lane pattern: the FP8 K block forms two
+// per-lane offsets once and reads each fragment at a constant offset from
+// them.
 __device__ __forceinline__ int row_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int chunk_pos(int chunk, int row) { return (chunk ^ row_key(row)) << 4; }
 
@@ -867,8 +868,10 @@ __global__ __launch_bounds__((WGN * WGM + NLD) * 64) void tile_kernel(Args a) {
 // Contiguous layout: each item's expert is found for all of the workgroup's
 // items at once, before any load.  Masked layout: the list holds only the
 // live tiles, expert by expert (ceil(masked_m[g] / BM) activation tiles by
-// the weight tiles); every workgroup builds the experts' offsets into it from
-// masked_m on the device, and finds an item's expert by binary search.
+// the weight tiles), up to 64 experts ordered by load so that each XCD's run
+// pairs a loaded expert with a light one; every workgroup builds the order
+// and the experts' offsets into the list from masked_m on the device, and
+// finds an item's expert by binary search.
 // ACT (fused SwiGLU, 256 x 128 tiles of interleaved gate/up rows): after a
 // tile's last block every wave, loaders included, takes one more barrier
 // for the epilogue's row maxima (swiglu_epilogue); the LDS ring is not used
