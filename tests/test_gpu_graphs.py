@@ -278,6 +278,52 @@ def test_two_streams_split_k_concurrently():
     announce("two streams: split-K results equal the serial ones")
 
 
+def test_host_threads_share_the_workspace():
+    """Four host threads, each with its own stream, call split-K decode and
+    tail-split large-M GEMMs at once (the binding releases the GIL in the
+    library call): the device workspace's lease serialises them on the GPU,
+    and every result equals the same call made alone."""
+    import threading
+    from parity_util import bits, sentinel_out
+    shapes = [(64, 2112, 7168, 8880), (128, 4096, 7168, 8881), (1100, 7400, 2048, 8882)]
+    ins, ref = [], []
+    for M, N, K, seed in shapes:
+        d = W.dense(seed, M, N, K)
+        args = (to_gpu(d["A"]), to_gpu(d["sa"]), to_gpu(d["B"]), to_gpu(d["sb"]))
+        D = sentinel_out((M, N))
+        fg.gemm_fp8_1x128_128x128_bf16(*args, D)
+        torch.cuda.synchronize()
+        ins.append((args, (M, N)))
+        ref.append(bits(D))
+    nthreads, rounds = 4, 6
+    streams = [torch.cuda.Stream() for _ in range(nthreads)]
+    outs = [[sentinel_out(mn) for _, mn in ins] for _ in range(nthreads)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(t):
+        try:
+            with torch.cuda.stream(streams[t]):
+                for r in range(rounds):
+                    for i in range(len(ins)):
+                        k = (i + t + r) % len(ins)  # threads start on different calls
+                        fg.gemm_fp8_1x128_128x128_bf16(*ins[k][0], outs[t][k])
+        except Exception as e:  # reported in the main thread
+            errors.append(repr(e))
+
+    announce(f"{nthreads} host threads, {rounds} rounds of {len(ins)} calls each")
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(nthreads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(nthreads):
+        for k in range(len(ins)):
+            assert (bits(outs[t][k]) == ref[k]).all(), f"thread {t}, call {k}"
+
+
 def test_graph_persistent_walk_calls():
     """The persistent walk under capture: a dense call with a tail split
     (its partials in the capture's own workspace), a contiguous call and
