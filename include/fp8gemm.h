@@ -126,7 +126,9 @@ int gemm_fp8_1x128_128x128_bf16_noalloc(const void *A, const float *sa, const vo
  *   for padding) is not written and keeps its previous contents.
  * Contract: M % 128 == 0, and each aligned 128-row block of A holds rows of
  * at most one expert (expert segments start at multiples of 128; padding
- * rows may sit anywhere).  Rows that break it are not written.
+ * rows may sit anywhere).  A block that breaks it is computed for the
+ * largest valid expert index among its rows; its rows of other experts are
+ * not written.
  */
 int grouped_contiguous(const void *A, const float *sa, const void *B, const float *sb, void *D,
                        int M, int N, int K, int G, void *stream, const int32_t *m_indices);

@@ -382,6 +382,50 @@ def test_contiguous_edge_cases():
     assert_close(out[valid], ref[valid], "contiguous edges")
 
 
+@pytest.mark.parametrize("walk", ["default", "0"])
+def test_contiguous_block_with_two_experts(walk, monkeypatch):
+    """A 128-row block that breaks the one-expert-per-block contract: it is
+    computed for the largest valid expert among its rows, whose rows match
+    the oracle; its rows of the other expert keep their contents.  FP8
+    (walked and one workgroup per tile) and BF16."""
+    if walk != "default":
+        monkeypatch.setenv("FP8GEMM_WALK", walk)
+    G, N, K = 4, 192, 384
+    idx = np.full(128 * 3, -1, np.int32)
+    idx[0:128] = 0
+    idx[128:188] = 1     # block 1: expert 1 ...
+    idx[188:250] = 3     # ... and expert 3 (the larger index: computed)
+    idx[256:300] = 2
+    M = idx.size
+    d = W.dense(4300, M, N, K)
+    B, sb = synth.grouped_weight(4301, G, N, K)
+    d.update(B=B, sb=sb, m_indices=idx, G=G)
+    announce(f"contiguous block with two experts, walk={walk}")
+    out = gpu_contig(d)
+    ref = oracle.grouped_contiguous(d["A"], d["sa"], B, sb, idx, np.full((M, N), SENTINEL, np.uint16))
+    skipped = np.zeros(M, bool)
+    skipped[128:188] = True
+    written = (idx >= 0) & (idx < G) & ~skipped
+    assert (out[~written] == SENTINEL).all(), "a row of the smaller expert or padding was written"
+    assert_close(out[written], ref[written], "contiguous two-expert block")
+    # BF16: the same rule
+    Ab = fg_bf16_bits(synth.normal(4302, M * K).reshape(M, K))
+    Bb = fg_bf16_bits(synth.normal(4303, G * N * K).reshape(G, N, K) * 0.5)
+    Db = sentinel_out((M, N))
+    fg.grouped_contiguous_bf16(to_gpu(Ab.view(np.int16)).view(torch.bfloat16),
+                               to_gpu(Bb.view(np.int16)).view(torch.bfloat16), to_gpu(idx), Db)
+    torch.cuda.synchronize()
+    got = bits(Db)
+    want = oracle.gemm_bf16("contiguous", Ab, Bb, idx, out=np.full((M, N), SENTINEL, np.uint16))
+    assert (got[~written] == SENTINEL).all(), "bf16: a skipped row was written"
+    assert_close(got[written], want[written], "bf16 contiguous two-expert block")
+
+
+def fg_bf16_bits(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def test_contiguous_routing_probe_exact():
     G, N, K, M = 8, 128, 128, 128 * 8
     B = np.zeros((G, N, K), np.uint8)
