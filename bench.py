@@ -356,7 +356,11 @@ def measure(torch, fg, workload, steps, warmup, dev, stream):
         units = dom["bytes"] / 1e9 if memory_bound else dom["flop"] / 1e12
         roof["profile"] = {"source": prof["source"], "trace_avg_us": prof["trace_avg_us"],
                            "frac": units / t / roof["peak"],
-                           "live_over_trace": dom["avg_us"] / prof["trace_avg_us"]}
+                           "live_over_trace": dom["avg_us"] / prof["trace_avg_us"],
+                           # the clock the call ran at in the profiled run (SQ busy cycles
+                           # per shader array over the traced duration) and its MFMA busy
+                           # fraction per cycle
+                           "sclk_ghz": prof.get("sclk_ghz"), "mfma_busy": prof.get("mfma_busy")}
     value = gbps if memory_bound else tflops
     return {"workload": WORKLOAD_TEXT[workload], "value": value,
             "unit": "GB/s" if memory_bound else "TFLOP/s", "ms_per_step": wall / steps * 1e3,
@@ -538,6 +542,8 @@ def summarize_profile(d, workload):
         if sq and i in sq:
             q = sq[i]
             busy = q["SQ_BUSY_CYCLES"] / n_arr  # per shader array: the launch's cycles
+            traffic[lab]["sclk_ghz"] = busy / (st.mean(durs) * 1e3)
+            traffic[lab]["mfma_busy"] = q["SQ_VALU_MFMA_BUSY_CYCLES"] / n_simd / busy
             sq_table.append(f"| {lab} | {q['SQ_VALU_MFMA_BUSY_CYCLES'] / n_simd / busy:.3f} | "
                             f"{q['SQ_LDS_BANK_CONFLICT'] / max(q['SQ_LDS_IDX_ACTIVE'], 1):.3f} | "
                             f"{busy / (st.mean(durs) * 1e3):.2f} |")
@@ -603,7 +609,8 @@ def profiled_call(kernel):
         if d.get("source_sha256") == sha and k:
             return {"traffic": {"bytes": k["fetch_bytes"] + k["write_bytes"], "fetch_bytes": k["fetch_bytes"],
                                 "write_bytes": k["write_bytes"], "source": os.path.basename(f)},
-                    "trace_avg_us": k.get("trace_avg_us"), "source": os.path.basename(f)}
+                    "trace_avg_us": k.get("trace_avg_us"), "source": os.path.basename(f),
+                    "sclk_ghz": k.get("sclk_ghz"), "mfma_busy": k.get("mfma_busy")}
     return None
 
 
