@@ -61,3 +61,24 @@ def test_workload_calls_cover_the_configured_shapes():
     assert set(bench.WORKLOAD_TEXT) >= {"decode", "prefill", "contiguous", "masked", "quant",
                                          "swiglu", "bf16", "small"}
     assert bench.MEMORY_BOUND == {"decode", "small", "masked", "quant"}
+
+
+def test_dispatch_order_maps_calls_and_timed_replays():
+    """The summarizer's reading of the bench's launch order: eager pass over
+    the rotation copies, warm-up and timed step replays (all calls in order),
+    then per call (reps + 1) graph replays of `copies` launches, the first
+    untimed; only those timed per-call replays count for the profile's
+    duration."""
+    line = {"per_call": [{}, {}], "config": {"rotating_copies": 3}, "warmup": 2, "steps": 20}
+    nc, copies, reps = 2, 3, 5  # reps = max(3, min(50, 20 // 4))
+    head = nc * (copies + 2 + 20)
+    n = head + nc * (reps + 1) * copies
+    calls = bench._call_of_dispatches(n, line)
+    timed = bench._timed_per_call(n, line)
+    assert calls[:head] == [i % nc for i in range(head)]
+    assert not any(timed[:head])
+    for c in range(nc):
+        block = range(head + c * (reps + 1) * copies, head + (c + 1) * (reps + 1) * copies)
+        assert all(calls[i] == c for i in block)
+        flags = [timed[i] for i in block]
+        assert flags == [False] * copies + [True] * (reps * copies)
