@@ -38,8 +38,9 @@
 //
 // The grouped layouts reuse the same body (GeekNews "성능 평가"): contiguous
 // tiles look up their expert from m_indices; masked tiles read the expert's
-// device-side row count and tiles past it exit before loading anything (or
-// the walk visits the live tiles only).  The fused SwiGLU + 1x128
+// device-side row count and tiles past it exit before loading anything (or,
+// for long K, the walk visits the live tiles only, the experts listed by
+// load).  The fused SwiGLU + 1x128
 // requantisation epilogue and a BF16 variant without scales run on the same
 // kernels.
 
