@@ -4,6 +4,7 @@ valid-row counts and size hints that the fixed cases do not cover.  Each
 case draws its shape from its own seed (90000 + case, printed before the
 call), so a failure names a reproducible case.  Tolerance and the written-row
 rules are those of the fixed parity tests."""
+import os
 import sys
 
 import numpy as np
@@ -16,7 +17,8 @@ import synth
 from parity_util import SENTINEL, assert_close, bits, sentinel_out, to_gpu
 
 pytestmark = pytest.mark.gpu
-CASES = 12
+# cases per family (a longer sweep: FP8GEMM_RANDOM_CASES=n)
+CASES = int(os.environ.get("FP8GEMM_RANDOM_CASES", "12"))
 DENSE_M = (1, 2, 7, 33, 64, 65, 100, 128, 129, 200, 255, 300, 513)
 
 
