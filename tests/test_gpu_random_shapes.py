@@ -1,6 +1,7 @@
-"""Seeded random shapes through the GEMM entry points and the quantiser,
-against the oracle: ragged M, N and K, group counts, padding patterns,
-valid-row counts and size hints that the fixed cases do not cover.  Each
+"""Seeded random shapes through the GEMM entry points, the fused SwiGLU calls
+and the quantiser, against the oracle: ragged M, N and K, group counts,
+padding patterns, valid-row counts and size hints that the fixed cases do
+not cover.  Each
 case draws its shape from its own seed (90000 + case, printed before the
 call), so a failure names a reproducible case.  Tolerance and the written-row
 rules are those of the fixed parity tests."""
@@ -176,3 +177,32 @@ def test_random_quantise(case):
     codes, scales = oracle.quantize_1x128(xb)
     assert (A.cpu().numpy() == codes).all()
     assert (sa.cpu().numpy().view(np.uint32) == scales.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_swiglu(case):
+    """the fused SwiGLU + 1x128 requantisation, contiguous and masked, under
+    the SwiGLU tests' own bounds (scales, codes within half a step plus the
+    fp32 error of h, at most 1% of codes differing)"""
+    from test_gpu_swiglu import compare_contig, compare_masked, gpu_contig, gpu_masked
+    r = rng(case, 5)
+    I, K = 128 * int(r.integers(1, 5)), 128 * int(r.integers(1, 40))
+    seed = 96000 + case
+    if case % 2 == 0:
+        G, blocks = int(r.integers(1, 6)), int(r.integers(1, 9))
+        idx = contiguous_layout(r, G, blocks)
+        M = idx.size
+        announce(f"random swiglu contiguous case {case}: G={G} rows={M} I={I} K={K} seed {seed}")
+        A, sa = synth.act(seed, M, K)
+        B, sb = synth.grouped_weight(seed + 1, G, 2 * I, K)
+        Yk, syk = gpu_contig(A, sa, B, sb, idx)
+        compare_contig(A, sa, B, sb, idx, Yk, syk, f"swiglu contiguous G={G} I={I} K={K}")
+    else:
+        G, M = int(r.integers(1, 7)), int(r.integers(1, 260))
+        mm = r.integers(-3, M + 4, size=G).astype(np.int32)
+        expected_m = int(r.choice([0, 64, 256]))
+        announce(f"random swiglu masked case {case}: G={G} M={M} I={I} K={K} seed {seed}")
+        A, sa = synth.grouped_act(seed, G, M, K)
+        B, sb = synth.grouped_weight(seed + 1, G, 2 * I, K)
+        Yk, syk = gpu_masked(A, sa, B, sb, mm, expected_m)
+        compare_masked(A, sa, B, sb, mm, Yk, syk, f"swiglu masked G={G} M={M} I={I} K={K}")
