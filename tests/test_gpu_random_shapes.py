@@ -1,10 +1,9 @@
 """Seeded random shapes through the GEMM entry points, the fused SwiGLU calls
 and the quantiser, against the oracle: ragged M, N and K, group counts,
 padding patterns, valid-row counts and size hints that the fixed cases do
-not cover.  Each
-case draws its shape from its own seed (90000 + case, printed before the
-call), so a failure names a reproducible case.  Tolerance and the written-row
-rules are those of the fixed parity tests."""
+not cover.  Each case draws its shape from its own seed (printed before the
+call), so a failure names a reproducible case.  Tolerance and the
+written-row rules are those of the fixed parity tests."""
 import os
 import sys
 
